@@ -1,0 +1,365 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something other than itself --
+the mathematics (fp64 exp, closed forms), brute force on tiny inputs, hand-worked examples under
+tests/golden/, invariants, or a special case that reduces to a library routine.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from expert_grouped_gemm_softmax_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def ulp32(x64: np.ndarray) -> np.ndarray:
+    """Spacing of fp32 numbers at |x| (x given in float64)."""
+    return np.spacing(np.abs(x64).astype(np.float32)).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# exp_ref: faithful (< 1 ulp of e^d) for every fp32 d in [-86, 0]; exact at 0; 0 below -86.
+# ----------------------------------------------------------------------------------------------
+def test_exp_ref_exhaustive_against_fp64_exp():
+    """Every fp32 d in [-86, 0] (about 1.1e9 values): exp_ref is faithful (< 1 ulp of e^d)."""
+    from concurrent.futures import ThreadPoolExecutor
+    lo = 0x80000000                                   # -0.0
+    hi = int(np.float32(-86.0).view(np.uint32))       # most negative covered value
+    step = 1 << 22
+
+    def chunk(start):
+        bits = np.arange(start, min(start + step, hi + 1), dtype=np.uint32)
+        d = bits.view(np.float32)
+        got = oracle.exp_ref(d).astype(np.float64)
+        ref = np.exp(d.astype(np.float64))
+        return float((np.abs(got - ref) / ulp32(ref)).max())
+
+    with ThreadPoolExecutor(8) as ex:
+        worst = max(ex.map(chunk, range(lo, hi + 1, step)))
+    assert worst < 1.0, worst
+
+
+def test_exp_ref_special_values():
+    d = np.array([0.0, -0.0, -86.0001, -100.0, -1e30], np.float32)
+    r = oracle.exp_ref(d)
+    assert r[0] == np.float32(1.0) and r[1] == np.float32(1.0)
+    assert np.all(r[2:] == 0.0)
+
+
+# ----------------------------------------------------------------------------------------------
+# Routing
+# ----------------------------------------------------------------------------------------------
+def _brute_topk(row: np.ndarray, k: int):
+    order = sorted(range(len(row)), key=lambda i: (-float(row[i]), i))
+    return order[:k]
+
+
+def _random_logits(rng, T, E, tie_quantum=None):
+    L = rng.standard_normal((T, E)).astype(np.float32) * np.float32(2.0)
+    if tie_quantum:
+        L = (np.rint(L / tie_quantum) * tie_quantum).astype(np.float32)
+    return L
+
+
+@pytest.mark.parametrize("T,E,k,tq", [(200, 8, 2, None), (100, 64, 10, None), (50, 512, 10, None),
+                                      (300, 16, 4, 0.25), (64, 512, 10, 0.5), (40, 33, 33, None),
+                                      (40, 1000, 1, None), (64, 70, 64, 0.25)])
+def test_route_matches_brute_force_sort(T, E, k, tq):
+    rng = np.random.default_rng(T * 1000 + E + k)
+    L = _random_logits(rng, T, E, tq)
+    L[0, :] = 0.0
+    L[1, ::2] = -0.0
+    ids, w = oracle.route(L, k)
+    for t in range(T):
+        assert list(ids[t]) == _brute_topk(L[t], k), t
+
+
+@pytest.mark.parametrize("T,E,k", [(500, 512, 10), (300, 8, 2), (200, 64, 6), (100, 32, 32)])
+def test_route_weights_match_fp64_renormalised_softmax(T, E, k):
+    """Weights against the fp64 softmax over all E experts, restricted to the selected ones and
+    renormalised.  Error budget, relative to w (u = 2^-24): the fp32 difference d_j = l_j - l_0
+    is rounded once (|d_j| u, which moves e^d_j by that relative amount), exp_ref is faithful
+    (2u), the k-term fp32 sum adds (k - 1) u on top of the worst term's error, the division u."""
+    rng = np.random.default_rng(7 + k)
+    L = _random_logits(rng, T, E)
+    ids, w = oracle.route(L, k)
+    sel = np.take_along_axis(L, ids, axis=1).astype(np.float64)
+    full = np.exp(L.astype(np.float64) - L.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    p = np.take_along_axis(full, ids, axis=1)
+    ref = p / p.sum(axis=1, keepdims=True)
+    u = 2.0 ** -24
+    d = np.abs(sel - sel[:, :1])
+    budget = (d + d.max(axis=1, keepdims=True) + 2 + 2 + (k - 1) + 1 + 1e-3) * u * ref
+    assert np.all(np.abs(w.astype(np.float64) - ref) <= budget)
+    # with the difference rounded to fp32 exactly as specified, only exp/sum/divide remain
+    d32 = (np.take_along_axis(L, ids, axis=1) - np.take_along_axis(L, ids[:, :1], axis=1)).astype(np.float64)
+    e = np.exp(d32)
+    ref32 = e / e.sum(axis=1, keepdims=True)
+    assert np.all(np.abs(w - ref32) <= (2 + 2 + (k - 1) + 1 + 1e-3) * u * ref32)
+    s = w.astype(np.float64).sum(axis=1)
+    assert np.abs(s - 1.0).max() <= (k + 8) * k * u
+    # selected slots in descending logit order
+    assert np.all(np.diff(sel, axis=1) <= 0)
+
+
+def test_route_special_cases():
+    # all-equal rows: ids 0..k-1, every weight the rounded 1/k
+    for k in (1, 2, 3, 7, 10):
+        L = np.full((3, 16), 1.25, np.float32)
+        ids, w = oracle.route(L, k)
+        assert np.all(ids == np.arange(k))
+        assert np.all(w == np.float32(1.0 / k))
+    # k = 1: weight exactly one
+    rng = np.random.default_rng(3)
+    ids, w = oracle.route(_random_logits(rng, 100, 40), 1)
+    assert np.all(w == 1.0)
+    # k = 2: w0 = 1 / (1 + exp(l1 - l0)) within 2 ulp
+    L = _random_logits(rng, 400, 12)
+    ids, w = oracle.route(L, 2)
+    l0 = np.take_along_axis(L, ids[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(L, ids[:, 1:], 1)[:, 0].astype(np.float64)
+    ref = 1.0 / (1.0 + np.exp(l1 - l0))
+    assert (np.abs(w[:, 0] - ref) / ulp32(ref)).max() <= 2.0
+
+
+def test_route_golden_worked_examples():
+    with open(os.path.join(GOLDEN, "route_worked.json")) as f:
+        fx = json.load(f)
+    for c in fx["cases"]:
+        L = np.array([c["logits"]], np.float32)
+        ids, w = oracle.route(L, c["k"])
+        assert list(ids[0]) == c["ids"], c
+        if "w" in c:
+            assert list(w[0]) == c["w"], c
+        else:
+            assert list(w[0].view(np.int32)) == c["w_bits"], c
+
+
+# ----------------------------------------------------------------------------------------------
+# Routing blob
+# ----------------------------------------------------------------------------------------------
+def test_blob_layout_and_round_trip():
+    rng = np.random.default_rng(11)
+    T, k = 37, 5
+    ids = rng.integers(0, 512, (T, k)).astype(np.int32)
+    wbits = rng.integers(-2**31, 2**31 - 1, (T, k), dtype=np.int64).astype(np.int32)
+    w = wbits.view(np.float32)                      # any bit pattern, NaN payloads included
+    blob = oracle.pack(ids, w)
+    assert blob.shape == (2, T, k)
+    assert np.array_equal(blob[0], ids)             # plane 0: ids
+    assert np.array_equal(blob[1], wbits)           # plane 1: weight bits
+    ids2, w2 = oracle.unpack(blob)
+    assert np.array_equal(ids2, ids) and np.array_equal(w2.view(np.int32), wbits)
+
+
+# ----------------------------------------------------------------------------------------------
+# Permutation
+# ----------------------------------------------------------------------------------------------
+def test_permute_golden_worked_examples():
+    with open(os.path.join(GOLDEN, "permute_worked.json")) as f:
+        fx = json.load(f)
+    for c in fx["cases"]:
+        ids = np.array(c["ids"], np.int32)
+        blob = oracle.pack(ids, np.zeros_like(ids, dtype=np.float32))
+        sp, off, pp = oracle.permute(blob, c["e_first"], c["e_local"])
+        assert list(off) == c["group_offsets"]
+        assert list(sp) == c["sorted_pairs"]
+        assert list(pp) == c["pair_pos"]
+
+
+@pytest.mark.parametrize("T,k,E,e_first,e_local", [(512, 10, 512, 0, 64), (300, 7, 64, 16, 16),
+                                                  (64, 2, 8, 0, 8), (100, 4, 512, 448, 64),
+                                                  (50, 3, 100, 97, 3), (1, 1, 4, 0, 4)])
+def test_permute_is_stable_counting_sort(T, k, E, e_first, e_local):
+    rng = np.random.default_rng(T + k + e_first)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    blob = oracle.pack(ids, np.zeros((T, k), np.float32))
+    sp, off, pp = oracle.permute(blob, e_first, e_local)
+    flat = ids.reshape(-1)
+    local = [p for p in range(T * k) if e_first <= flat[p] < e_first + e_local]
+    # python's sort is stable: equal keys keep ascending p
+    ref = sorted(local, key=lambda p: flat[p] - e_first)
+    assert list(sp) == ref
+    cnt = np.bincount(flat[local] - e_first, minlength=e_local) if local else np.zeros(e_local, int)
+    assert list(off) == [0] + list(np.cumsum(cnt))
+    assert off[-1] == len(local) and np.all(np.diff(off) >= 0)
+    # pair_pos is the inverse of sorted_pairs, -1 elsewhere
+    assert np.all(pp[sp] == np.arange(len(sp)))
+    mask = np.ones(T * k, bool)
+    mask[sp] = False
+    assert np.all(pp[mask] == -1)
+    if e_first == 0 and e_local >= E:
+        assert len(sp) == T * k
+
+
+# ----------------------------------------------------------------------------------------------
+# Expert FFN and combine
+# ----------------------------------------------------------------------------------------------
+def _dense_f64(inp, cfg, name):
+    a = inp[name]
+    if cfg.wfmt == "int4" and name in ("w_gate", "w_up", "w_down"):
+        words = a.view(np.uint32)
+        E_, Kb, N = words.shape
+        q = np.empty((E_, Kb * 8, N), np.float64)
+        for i in range(8):
+            nib = ((words >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int64)
+            q[:, i::8, :] = np.where(nib >= 8, nib - 16, nib)
+        s = W.bf16_bits_to_f32(inp[name + "_scale"]).astype(np.float64)
+        return q * np.repeat(s, cfg.group_size, axis=1)
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _brute_layer(inp, cfg, ids, w):
+    """Dense evaluation: every local expert on every token, times a dense gate matrix that holds
+    the renormalised weight at each selected local entry and 0 elsewhere."""
+    x = _dense_f64(inp, cfg, "x")
+    Wg, Wu, Wd = (_dense_f64(inp, cfg, n) for n in ("w_gate", "w_up", "w_down"))
+    G = np.zeros((cfg.T, cfg.e_local))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            le = ids[t, j] - cfg.e_first
+            if 0 <= le < cfg.e_local:
+                G[t, le] += float(w[t, j])
+    y = np.zeros((cfg.T, cfg.H))
+    for e in range(cfg.e_local):
+        out = (_silu(x @ Wg[e]) * (x @ Wu[e])) @ Wd[e]
+        y += G[:, e:e + 1] * out
+    if cfg.shared_I:
+        Sg, Su, Sd = (_dense_f64(inp, cfg, n) for n in ("shared_gate", "shared_up", "shared_down"))
+        y += (_silu(x @ Sg) * (x @ Su)) @ Sd
+    return y
+
+
+def _tiny(**kw):
+    base = dict(name="pin", T=24, H=32, E=12, k=3, I=16, e_first=0, e_local=12, act="f32")
+    base.update(kw)
+    return W.MoEConfig(**base)
+
+
+@pytest.mark.parametrize("cfg", [
+    _tiny(),
+    _tiny(e_first=4, e_local=5),
+    _tiny(act="bf16", e_first=2, e_local=8, shared_I=24),
+    _tiny(act="bf16", wfmt="int4", group_size=8, H=64, I=32, E=16, e_local=16, k=4),
+    _tiny(act="bf16", wfmt="int4", group_size=64, H=64, I=64, e_first=3, e_local=6),
+    W.CONFIGS["tiny"],
+])
+def test_layer_matches_dense_brute_force(cfg):
+    inp = W.make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], cfg.k)
+    y = oracle.layer(inp, cfg, ids, w, threads=4)
+    ref = _brute_layer(inp, cfg, ids, w)
+    assert np.linalg.norm(y - ref) <= 1e-12 * np.linalg.norm(ref)
+
+
+def test_layer_identical_experts_reduce_to_one_ffn():
+    cfg = _tiny(e_local=12)
+    inp = W.make_inputs(cfg)
+    for n in ("w_gate", "w_up", "w_down"):
+        inp[n] = np.ascontiguousarray(np.broadcast_to(inp[n][:1], inp[n].shape))
+    ids, w = oracle.route(inp["logits"], cfg.k)
+    y = oracle.layer(inp, cfg, ids, w)
+    x = inp["x"].astype(np.float64)
+    ffn = (_silu(x @ inp["w_gate"][0]) * (x @ inp["w_up"][0])) @ inp["w_down"][0]
+    # the weights sum to one within k fp32 roundings
+    assert np.abs(y - ffn).max() <= cfg.k * 2.0 ** -23 * np.abs(ffn).max() * 4
+
+
+def test_layer_single_expert_is_textbook_swiglu_mlp():
+    import torch
+    cfg = _tiny(E=1, e_local=1, k=1, T=9, H=40, I=24)
+    inp = W.make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], 1)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    y = oracle.layer(inp, cfg, ids, w)
+    x = torch.from_numpy(inp["x"].astype(np.float64))
+    g, u, d = (torch.from_numpy(inp[n][0].astype(np.float64)) for n in ("w_gate", "w_up", "w_down"))
+    ref = (torch.nn.functional.silu(x @ g) * (x @ u)) @ d
+    assert np.allclose(y, ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def test_layer_zero_and_scaled_down_projection():
+    cfg = _tiny(shared_I=8)
+    inp = W.make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], cfg.k)
+    base = oracle.layer(inp, cfg, ids, w)
+    # no shared expert, doubled down projection: output doubles exactly
+    cfg0 = cfg.with_(shared_I=0)
+    y1 = oracle.layer(inp, cfg0, ids, w)
+    inp2 = dict(inp, w_down=inp["w_down"] * np.float32(2.0))
+    assert np.array_equal(oracle.layer(inp2, cfg0, ids, w), 2.0 * y1)
+    # zero down projection: only the shared expert remains
+    inp0 = dict(inp, w_down=np.zeros_like(inp["w_down"]))
+    y0 = oracle.layer(inp0, cfg, ids, w)
+    x = inp["x"].astype(np.float64)
+    sh = (_silu(x @ inp["shared_gate"]) * (x @ inp["shared_up"])) @ inp["shared_down"]
+    assert np.allclose(y0, sh, rtol=1e-13, atol=1e-15)
+    assert np.allclose(base - y0, y1, rtol=1e-12, atol=1e-13)
+
+
+def test_layer_token_subset_equals_full_rows():
+    cfg = _tiny(act="bf16", e_first=1, e_local=7)
+    inp = W.make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], cfg.k)
+    full = oracle.layer(inp, cfg, ids, w)
+    toks = np.array([5, 0, 23, 11], np.int32)
+    assert np.array_equal(oracle.layer(inp, cfg, ids, w, tokens=toks, threads=3), full[toks])
+
+
+# ----------------------------------------------------------------------------------------------
+# int4 and bf16 conversions
+# ----------------------------------------------------------------------------------------------
+def test_int4_nibbles_round_trip_every_value_and_position():
+    for i in range(8):
+        for v in range(-8, 8):
+            word = (v & 0xF) << (4 * i)
+            assert oracle.int4_nibble(word, i) == v
+            for j in range(8):
+                if j != i:
+                    assert oracle.int4_nibble(word, j) == 0
+
+
+def test_int4_expand_matrix_by_hand_and_exact_products():
+    K, N, gs = 16, 3, 8
+    rng = np.random.default_rng(5)
+    q = rng.integers(-8, 8, (K, N))
+    s_bits = W.f32_to_bf16_bits(rng.uniform(0.01, 3.0, (K // gs, N)).astype(np.float32))
+    words = W.pack_int4(q)
+    got = oracle.expand_matrix(words[None], s_bits[None], oracle.INT4, oracle.BF16, K, N, gs, 0)
+    s = W.bf16_bits_to_f32(s_bits).astype(np.float64)
+    assert np.array_equal(got, q * np.repeat(s, gs, axis=0))
+    # q * s is exact in fp32 (<= 4-bit times 8-bit significands)
+    qq = np.arange(-8, 8, dtype=np.float32)[:, None]
+    ss = W.bf16_bits_to_f32(rng.integers(0x3000, 0x4800, 64).astype(np.uint16))[None, :]
+    assert np.array_equal((qq * ss).astype(np.float64), qq.astype(np.float64) * ss.astype(np.float64))
+
+
+def test_int4_quantiser_error_bound():
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal((256, 40)).astype(np.float32) / 16
+    w[:128, 0] = 0.0                                            # an all-zero group
+    q, s_bits = W.quantize_int4_sym(w, 128)
+    words = W.pack_int4(q)
+    deq = oracle.expand_matrix(words[None], s_bits[None], oracle.INT4, oracle.BF16, 256, 40, 128, 0)
+    s = np.repeat(W.bf16_bits_to_f32(s_bits).astype(np.float64), 128, axis=0)
+    unclamped = (q > -8) & (q < 7)
+    assert np.all(np.abs(w - deq)[unclamped] <= s[unclamped] / 2 * (1 + 2.0 ** -20))
+    assert np.all(deq[:128, 0] == 0.0)
+
+
+def test_bf16_conversion_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = W.bf16_bits_to_f32(bits).astype(np.float64)
+    got = np.array([oracle.bf16_to_double(b) for b in bits[::97]])
+    r = ref[::97]
+    fin = np.isfinite(r)
+    assert np.array_equal(got[fin], r[fin])
