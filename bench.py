@@ -1,0 +1,236 @@
+"""Benchmark: one device's share of a routed MoE layer on one MI355X.
+
+A step is one pass of the whole path (route -> pack -> permute -> gate/up GEMM + SwiGLU -> down
+GEMM [-> shared expert] -> combine) over one batch of synthetic inputs already resident in HBM.
+Prints ONE JSON line.  The default workload is the decode-shaped EP share (T=512 tokens, hidden
+4096, experts 0-63 of 512 local, top-10, intermediate 1024, bf16).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calibration      # plain device copy of known size (HBM counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed token-expert pairs/s + % of HBM/MFMA roofline, one device's MoE layer"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix peak
+FP32_PEAK_TFS = 157.3          # MI355X fp32 vector peak
+
+DESCR = {
+    "tiny": "tiny MoE layer, all local: T=64, H=256, 8 experts, top-2, I=128, fp32",
+    "decode": "decode-shaped EP share: T=512, H=4096, experts 0-63 of 512 local, top-10, I=1024, bf16",
+    "prefill": "prefill-shaped EP share: T=8192, H=4096, experts 0-63 of 512 local, top-10, I=1024, bf16",
+    "skewed_shared": "Zipf-skewed routing + shared SwiGLU expert: T=8192, H=4096, 64 of 512 local, "
+                     "top-10, I=1024, shared I=1024, bf16",
+    "w4a16": "W4A16 prefill EP share: T=8192, H=4096, 64 of 512 local, top-10, I=1024, int4 weights "
+             "(group 128, bf16 scales), bf16 activations",
+}
+
+
+def kernel_source_hash() -> str:
+    from expert_grouped_gemm_softmax_amd.build import sources
+    h = hashlib.sha256()
+    for p in sources() + [os.path.join(ROOT, "expert_grouped_gemm_softmax_amd", "csrc", "common.h")]:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when absent or taken on
+    different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("kernel_src") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def gemm_work(cfg, n_loc: int, nonempty: int, op: str):
+    """Algorithmic FLOPs and HBM bytes of one grouped-GEMM launch: every weight byte of the
+    experts that received pairs read once, activations read once, outputs written once."""
+    H, I, T = cfg.H, cfg.I, cfg.T
+    act = 2 if cfg.act == "bf16" else 4
+    if cfg.wfmt == "int4":
+        wbytes = lambda K, N: K * N // 2 + (K // cfg.group_size) * N * 2
+    else:
+        wbytes = lambda K, N: K * N * act
+    if op == "gate_up":
+        flops = 4.0 * H * I * n_loc
+        byts = nonempty * 2 * wbytes(H, I) + T * H * act + n_loc * I * act
+    else:
+        flops = 2.0 * H * I * n_loc
+        byts = nonempty * wbytes(I, H) + n_loc * I * act + n_loc * H * act
+    return flops, byts
+
+
+def roofline(cfg, flops: float, byts: float, seconds: float):
+    peak_f = MFMA_BF16_PEAK_TFS if cfg.act == "bf16" else FP32_PEAK_TFS
+    t_hbm = byts / (HBM_PEAK_GBS * 1e9)
+    t_mat = flops / (peak_f * 1e12)
+    if t_hbm >= t_mat:
+        a = byts / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4)}
+    a = flops / seconds / 1e12
+    return {"bound": "mfma" if cfg.act == "bf16" else "alu", "achieved": round(a, 1), "peak": peak_f,
+            "unit": "TFLOP/s", "frac": round(a / peak_f, 4)}
+
+
+def cpu_baseline(cfg, inp, budget_s: float):
+    """The CPU oracle on a bounded sample of the same workload's tokens (whole path for those
+    tokens: routing, blob, permutation, expert FFNs and combine)."""
+    import numpy as np
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        ids, w = oracle.route(inp["logits"][tokens], cfg.k)
+        blob = oracle.pack(ids, w)
+        sp, off, pp = oracle.permute(blob, cfg.e_first, cfg.e_local)
+        sub = dict(inp, x=inp["x"][tokens])
+        oracle.layer(sub, cfg.with_(T=len(tokens)), ids, w, threads=threads)
+        return time.perf_counter() - t0, int(off[-1])
+
+    rng = np.random.default_rng(1)
+    probe = np.sort(rng.choice(cfg.T, size=min(cfg.T, 2 * threads), replace=False))
+    t_probe, _ = run(probe)
+    n = int(min(cfg.T, max(len(probe), len(probe) * budget_s / max(t_probe, 1e-6))))
+    tokens = np.sort(rng.choice(cfg.T, size=n, replace=False))
+    secs, pairs = run(tokens)
+    return {"value": round(pairs / secs, 2), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {cfg.T} tokens drawn uniformly (seed 1), {pairs} local pairs, "
+                      f"{secs:.1f} s on {threads} host threads"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+    from expert_grouped_gemm_softmax_amd import workloads as W
+    from expert_grouped_gemm_softmax_amd.layer import MoELayer, upload
+
+    cfg = W.CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    inp = W.make_inputs(cfg, threads=16)
+    x, logits, wts = upload(inp, cfg, torch.device("cuda:0"))
+    layer = MoELayer.from_config(cfg, wts)
+    b = layer.buffers(cfg.T, x.device)
+    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        layer.forward(x, logits)
+    torch.cuda.synchronize()
+    off = b.group_offsets.cpu().numpy()
+    n_loc = int(off[-1])
+    nonempty = int((np.diff(off) > 0).sum())
+
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    names = ["route_pack_permute", "gate_up", "down"] + (["shared"] if cfg.shared_I else []) + ["combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        layer.step_route(logits, b)
+        e[1].record(stream)
+        layer.step_gate_up(x, b)
+        e[2].record(stream)
+        layer.step_down(x, b)
+        e[3].record(stream)
+        j = 4
+        if cfg.shared_I:
+            layer.step_shared(x, b)
+            e[j].record(stream)
+            j += 1
+        layer.step_combine(b)
+        e[j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    per_kernel = {n: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(K)] for j, n in enumerate(names)}
+    step_us = np.array([ev[i][0].elapsed_time(ev[i][-1]) * 1e3 for i in range(K)])
+    ms_per_step = wall / K * 1e3
+    value = n_loc / (ms_per_step / 1e3)
+
+    gu_us = float(np.mean(per_kernel["gate_up"]))
+    flops, byts = gemm_work(cfg, n_loc, nonempty, "gate_up")
+    roof = roofline(cfg, flops, byts, gu_us * 1e-6)
+    roof["kernel"] = "grouped GEMM gate/up + SwiGLU"
+    roof["algorithmic_bytes"] = int(byts)
+    roof["algorithmic_flops"] = int(flops)
+    roof["traffic"] = measured_traffic(args.workload, "gate_up")
+    dn_us = float(np.mean(per_kernel["down"]))
+    dflops, dbytes = gemm_work(cfg, n_loc, nonempty, "down")
+    layer_flops = flops + dflops
+    layer_bytes = byts + dbytes
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "pairs/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic: seeded normal activations, random-init expert weights, fp32 router logits",
+        "config": {"workload": DESCR[args.workload], "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "e_local": cfg.e_local, "weights": cfg.wfmt, "shared_I": cfg.shared_I},
+        "roofline": roof,
+        "n_local_pairs": n_loc,
+        "latency_us": {"median": round(float(np.median(step_us)), 1),
+                       "p10": round(float(np.percentile(step_us, 10)), 1),
+                       "p90": round(float(np.percentile(step_us, 90)), 1)},
+        "kernels_us": {n: round(float(np.mean(v)), 1) for n, v in per_kernel.items()},
+        "down_roofline": roofline(cfg, dflops, dbytes, dn_us * 1e-6),
+        "gemm_pair_roofline": roofline(cfg, layer_flops, layer_bytes, (gu_us + dn_us) * 1e-6),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

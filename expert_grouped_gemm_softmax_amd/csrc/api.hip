@@ -1,0 +1,109 @@
+// C ABI of libmoe_mi355x.so: host-side validation and dispatch.  Every entry point validates its
+// arguments before making any HIP call, so invalid calls are rejected without a GPU and without
+// enqueueing work.
+#include <atomic>
+#include <climits>
+
+#include "common.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+}  // namespace moe
+
+namespace {
+
+inline bool fits_i32(long long v) { return v >= 0 && v < (long long)INT_MAX; }
+inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+MOE_API moe_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                             void* stream) {
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
+  if (!fits_i32((long long)T * E)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_w, as_stream(stream)));
+}
+
+MOE_API moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T, int k,
+                                    int32_t* blob, void* stream) {
+  if (!topk_ids || !topk_w || !blob) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_pack(topk_ids, topk_w, T, k, blob, as_stream(stream)));
+}
+
+MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
+                               int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
+                               void* stream) {
+  if (!blob || !sorted_pairs || !group_offsets || !pair_pos) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
+  if (e_local < 1 || e_local > 1024 || e_first < 0 || !fits_i32((long long)e_first + e_local))
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_permute(blob, T, k, e_first, e_local, sorted_pairs, group_offsets,
+                                      pair_pos, as_stream(stream)));
+}
+
+MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  if (a->op != MOE_OP_GATE_UP_SWIGLU && a->op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
+  if (a->act_dtype != MOE_DT_F32 && a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP) return MOE_ERR_UNSUPPORTED;
+  if (a->reserved != 0) return MOE_ERR_INVALID_ARG;
+  const bool gu = a->op == MOE_OP_GATE_UP_SWIGLU;
+  if (!a->a || !a->group_offsets || !a->w0 || !a->out) return MOE_ERR_INVALID_ARG;
+  if (gu ? !a->w1 : a->w1 != nullptr) return MOE_ERR_INVALID_ARG;
+  if (a->K < 64 || a->K % 64 != 0 || a->N < 64) return MOE_ERR_INVALID_ARG;
+  if (a->N % (gu ? 64 : 128) != 0) return MOE_ERR_INVALID_ARG;
+  if (a->n_groups < 1 || a->n_groups > 1024) return MOE_ERR_INVALID_ARG;
+  if (a->rows_cap < 1 || a->a_rows < 1 || a->row_div < 1 || a->m_hint < 0) return MOE_ERR_INVALID_ARG;
+  if (!a->row_index && a->a_rows < a->rows_cap) return MOE_ERR_INVALID_ARG;
+  if (a->wfmt == MOE_W_INT4_SYM_GROUP) {
+    if (a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+    if (a->group_size < 64 || a->group_size % 64 != 0 || a->K % a->group_size != 0)
+      return MOE_ERR_UNSUPPORTED;
+    if (!a->s0 || (gu && !a->s1)) return MOE_ERR_INVALID_ARG;
+  } else if (a->group_size != 0 || a->s0 || a->s1) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return from_hip(moe::launch_grouped_gemm(*a, as_stream(stream)));
+}
+
+MOE_API moe_status moe_combine(const void* expert_out, int expert_rows, int act_dtype, const int32_t* blob,
+                               const int32_t* pair_pos, const void* shared_out, int T, int k, int H,
+                               void* y, int y_dtype, void* stream) {
+  if (!expert_out || !blob || !pair_pos || !y) return MOE_ERR_INVALID_ARG;
+  if (act_dtype != MOE_DT_F32 && act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (expert_rows < 1 || T < 1 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (!fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_combine(expert_out, act_dtype, blob, pair_pos, shared_out, T, k, H,
+                                      expert_rows, y, y_dtype, as_stream(stream)));
+}

@@ -1,0 +1,439 @@
+// Grouped GEMM over the local experts for gfx950: the fused gate/up projection with SwiGLU, and
+// the down projection.
+//
+// "Systems engineering playbook: optimizing Qwen 3.5-397B MoE on Ironwood (TPU7x)": the grouped
+// GEMM building block (executive summary) over 64 local experts of intermediate size 1024
+// (sections 1 and 3); decode batches stream every expert weight from HBM, prefill batches are
+// bound by the matrix units (section 2).  "vLLM TPU Inference v0.31.0" (4-bit weight scope): int4
+// weights stay packed in HBM and only the tiles in use are dequantised on chip.
+//
+// Design (MI355X):
+//  - Work unit = tile (expert e, m-tile of BM rows of that expert, n-tile of BN output columns).
+//    Tiles are numbered expert by expert, n-tile major and m-tile minor, so consecutive tiles
+//    reuse one weight slab.  Each workgroup derives the tile table from group_offsets in LDS, so
+//    the number of local pairs never goes through the host.
+//  - Persistent grid, a multiple of 8 workgroups.  Workgroup b runs on XCD b % 8; the tiles are
+//    cut into 8 contiguous ranges and XCD x's workgroups walk range x, so tiles sharing a weight
+//    slab or activation rows share one L2.
+//  - Activation rows are gathered (row_index / row_div) straight into LDS, 16 bytes per lane.
+//  - Dense bf16 weights W[e][K][N] are N-contiguous while MFMA wants 8 consecutive k per lane: each
+//    lane loads an R x 8 block (R k-rows, 16 bytes each), transposes it in registers with v_perm
+//    and writes it K-contiguous into LDS ([n][k], padded rows).  int4 words already hold 8
+//    consecutive k of one column: they are dequantised (q * scale, rounded to bf16) straight
+//    into the same [n][k] LDS layout.
+//  - v_mfma_f32_16x16x32_bf16 with fp32 accumulators; SwiGLU fused in the epilogue (each lane
+//    holds the gate and the up value of the same output element).
+//  - Global loads for chunk c+1 are issued before the MFMAs of chunk c (register prefetch).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+struct GemmParams {
+  const void* a;
+  const int32_t* row_index;
+  const int32_t* group_offsets;
+  const void* w0;
+  const void* w1;
+  const void* s0;
+  const void* s1;
+  void* out;
+  int K, N, n_groups, rows_cap, a_rows, row_div, group_size;
+};
+
+// ---------------------------------------------------------------------------------------------
+// Tile table: s_tstart[e] = first tile of group e, s_tstart[n_groups] = total tiles;
+// s_goff[e] = clamped row offset of group e.  Built by wave 0 in chunks of 64 groups.
+// ---------------------------------------------------------------------------------------------
+__device__ void build_tile_table(const GemmParams& p, int BM, int tiles_n, int* s_tstart, int* s_goff) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int carry = 0;
+  for (int c0 = 0; c0 < p.n_groups; c0 += 64) {
+    const int e = c0 + lane;
+    int tiles = 0;
+    if (e < p.n_groups) {
+      int lo = p.group_offsets[e], hi = p.group_offsets[e + 1];
+      lo = min(max(lo, 0), p.rows_cap);
+      hi = min(max(hi, lo), p.rows_cap);
+      s_goff[e] = lo;
+      if (e == p.n_groups - 1) s_goff[p.n_groups] = hi;
+      tiles = ((hi - lo + BM - 1) / BM) * tiles_n;
+    }
+    int incl = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (e < p.n_groups) s_tstart[e] = carry + incl - tiles;
+    carry += __shfl(incl, 63);
+  }
+  if (lane == 0) s_tstart[p.n_groups] = carry;
+}
+
+// Largest e with s_tstart[e] <= tile (groups with no tiles are skipped naturally).
+__device__ __forceinline__ int find_group(const int* s_tstart, int n_groups, int tile) {
+  int lo = 0, hi = n_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_tstart[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct TileIter {
+  int next, end, step;
+};
+
+// XCD-aware static schedule over [0, total).
+__device__ __forceinline__ TileIter tile_range(int total) {
+  const int G = gridDim.x;               // a multiple of 8
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, gx = G >> 3;
+  const int per = (total + 7) >> 3;
+  const int beg = xcd * per;
+  return {beg + j, min(total, beg + per), gx};
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return __fdividef(g, 1.0f + __expf(-g)) * u;
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 MFMA kernel
+// ---------------------------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, bool GU, bool Q4>
+struct Cfg {
+  static constexpr int KC = 64;                     // K chunk per LDS stage
+  static constexpr int NW = GU ? 2 : 1;             // weight matrices
+  static constexpr int LDK = KC + 8;                // padded LDS row (bf16 elements): 144 bytes
+  static constexpr int A_ELEMS = BM * LDK;
+  static constexpr int B_ELEMS = NW * BN * LDK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;   // u16 elements
+  static constexpr int A_LOADS = BM * (KC / 8) / 256;          // 16-byte A chunks per thread
+  // B units per thread: a dense R x 8 block or one 16-byte row of 4 int4 words, 32 weights each
+  static constexpr int B_UNITS = NW * KC * BN / 32 / 256;
+  static constexpr int R = 4;                       // dense: k-rows per transposed block
+  static constexpr int MT = BM / WM / 16;
+  static constexpr int NTL = BN / WN / 16;
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(A_LOADS >= 1 && BM * (KC / 8) % 256 == 0, "A tile split");
+  static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * 256) == 0, "B tile split");
+  static_assert(MT >= 1 && NTL >= 1, "wave tile");
+  static size_t lds_bytes(int n_groups) { return STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
+};
+
+template <int BM, int BN, int WM, int WN, bool GU, bool Q4>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
+  using C = Cfg<BM, BN, WM, WN, GU, Q4>;
+  constexpr int KC = C::KC, NW = C::NW, LDK = C::LDK;
+  extern __shared__ __attribute__((aligned(16))) u16 smem[];
+  u16* sA = smem;
+  u16* sB = smem + C::A_ELEMS;
+  int* s_tstart = reinterpret_cast<int*>(smem + C::STAGE);
+  int* s_goff = s_tstart + (p.n_groups + 1);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = p.N / BN;
+  const int nK = p.K / KC;
+
+  build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
+  __syncthreads();
+  const int total = s_tstart[p.n_groups];
+  const TileIter it = tile_range(total);
+
+  const u16* A = static_cast<const u16*>(p.a);
+  u16* O = static_cast<u16*>(p.out);
+
+  for (int tile = it.next; tile < it.end; tile += it.step) {
+    const int e = find_group(s_tstart, p.n_groups, tile);
+    const int g0 = s_goff[e], g1 = s_goff[e + 1];
+    const int mtiles = (g1 - g0 + BM - 1) / BM;
+    const int local = tile - s_tstart[e];
+    const int mt = local % mtiles, nt = local / mtiles;
+    const int row0 = g0 + mt * BM;
+    const int rows = min(BM, g1 - row0);
+    const int n0 = nt * BN;
+
+    // ---- per-thread global source pointers -------------------------------------------------
+    const u16* a_src[C::A_LOADS];
+    int a_lds[C::A_LOADS];
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (KC / 8), kc8 = c % (KC / 8);
+      const int rr = row0 + min(r, rows - 1);              // pad rows repeat a valid row
+      int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
+      src = min(max(src, 0), p.a_rows - 1);
+      a_src[i] = A + (size_t)src * p.K + kc8 * 8;
+      a_lds[i] = r * LDK + kc8 * 8;
+    }
+
+    // Dense: unit = R x 8 block (R k-rows, 8 columns); int4: unit = one 16-byte row of 4 words.
+    const char* b_src[C::B_UNITS];
+    const u16* s_src[C::B_UNITS];
+    int b_lds[C::B_UNITS];
+#pragma unroll
+    for (int i = 0; i < C::B_UNITS; ++i) {
+      const int u = tid + 256 * i;
+      if constexpr (!Q4) {
+        constexpr int per_m = (KC / C::R) * (BN / 8);
+        const int m = u / per_m, v = u % per_m;
+        const int nb = v % (BN / 8), kb = v / (BN / 8);
+        const u16* W = static_cast<const u16*>(m == 0 ? p.w0 : p.w1);
+        b_src[i] = reinterpret_cast<const char*>(W + ((size_t)e * p.K + kb * C::R) * p.N + n0 + nb * 8);
+        b_lds[i] = (m * BN + nb * 8) * LDK + kb * C::R;
+        s_src[i] = nullptr;
+      } else {
+        constexpr int per_m = (KC / 8) * (BN / 4);
+        const int m = u / per_m, v = u % per_m;
+        const int nq = v % (BN / 4), kw = v / (BN / 4);
+        const int32_t* Wq = static_cast<const int32_t*>(m == 0 ? p.w0 : p.w1);
+        const u16* S = static_cast<const u16*>(m == 0 ? p.s0 : p.s1);
+        b_src[i] = reinterpret_cast<const char*>(Wq + ((size_t)e * (p.K / 8) + kw) * p.N + n0 + nq * 4);
+        s_src[i] = S + (size_t)e * (p.K / p.group_size) * p.N + n0 + nq * 4;
+        b_lds[i] = (m * BN + nq * 4) * LDK + kw * 8;
+      }
+    }
+
+    u32x4 ra[C::A_LOADS];
+    u32x4 rb[C::B_UNITS][Q4 ? 1 : C::R];
+    u32x2 rs[C::B_UNITS];
+
+    auto load_chunk = [&](int kc) {
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i)
+        ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kc * KC);
+#pragma unroll
+      for (int i = 0; i < C::B_UNITS; ++i) {
+        if constexpr (!Q4) {
+#pragma unroll
+          for (int r = 0; r < C::R; ++r)
+            rb[i][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                b_src[i] + ((size_t)kc * KC + r) * p.N * sizeof(u16)));
+        } else {
+          rb[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              b_src[i] + (size_t)kc * (KC / 8) * p.N * sizeof(int32_t)));
+          const int grp = (kc * KC) / p.group_size;
+          rs[i] = *reinterpret_cast<const u32x2*>(s_src[i] + (size_t)grp * p.N);
+        }
+      }
+    };
+
+    auto store_chunk = [&]() {
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + a_lds[i]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < C::B_UNITS; ++i) {
+        if constexpr (!Q4) {
+          // rb[i][r] = row r (k), dwords d = columns (2d, 2d+1).  Column c gets k-rows 0..3.
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const int d = c >> 1;
+            uint32_t lo, hi;
+            if (c & 1) {
+              lo = pack_hi16(rb[i][0][d], rb[i][1][d]);
+              hi = pack_hi16(rb[i][2][d], rb[i][3][d]);
+            } else {
+              lo = pack_lo16(rb[i][0][d], rb[i][1][d]);
+              hi = pack_lo16(rb[i][2][d], rb[i][3][d]);
+            }
+            *reinterpret_cast<u32x2*>(sB + b_lds[i] + c * LDK) = u32x2{lo, hi};
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t word = rb[i][0][c];
+            const uint32_t sbits = (c & 1) ? (rs[i][c >> 1] >> 16) : (rs[i][c >> 1] & 0xffffu);
+            const float s = __uint_as_float(sbits << 16);
+            uint32_t q[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const int q0 = ((int)(word << (28 - 8 * h))) >> 28;        // nibble 2h
+              const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
+              q[h] = pack_bf16x2((float)q0 * s, (float)q1 * s);
+            }
+            *reinterpret_cast<u32x4*>(sB + b_lds[i] + c * LDK) = u32x4{q[0], q[1], q[2], q[3]};
+          }
+        }
+      }
+    };
+
+    f32x4 acc[NW][C::MT][C::NTL];
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int arow = wm * (BM / WM) + (lane & 15);
+    const int bcol = wn * (BN / WN) + (lane & 15);
+    const int kofs = (lane >> 4) * 8;
+
+    load_chunk(0);
+    for (int kc = 0; kc < nK; ++kc) {
+      store_chunk();
+      __syncthreads();
+      if (kc + 1 < nK) load_chunk(kc + 1);
+#pragma unroll
+      for (int ks = 0; ks < KC; ks += 32) {
+        bf16x8 av[C::MT];
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+          av[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 16) * LDK + ks + kofs);
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+#pragma unroll
+          for (int j = 0; j < C::NTL; ++j) {
+            const bf16x8 bv =
+                *reinterpret_cast<const bf16x8*>(sB + (m * BN + bcol + j * 16) * LDK + ks + kofs);
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i)
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
+          }
+      }
+      __syncthreads();
+    }
+
+    // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile ----------
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+          const int col = wn * (BN / WN) + j * 16 + (lane & 15);
+          if (row < rows) {
+            float v;
+            if constexpr (GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
+            else v = acc[0][i][j][r];
+            O[(size_t)(row0 + row) * p.N + n0 + col] = f32_to_bf16(v);
+          }
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 kernel (vector ALU): 32 x 64 tiles, K chunks of 32 staged in LDS.
+// ---------------------------------------------------------------------------------------------
+template <bool GU>
+__global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
+  constexpr int BM = 32, BN = 64, KC = 32, NW = GU ? 2 : 1;
+  __shared__ float sA[BM][KC + 1];
+  __shared__ float sB[NW][KC][BN];
+  extern __shared__ int tbl[];
+  int* s_tstart = tbl;
+  int* s_goff = tbl + (p.n_groups + 1);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tiles_n = p.N / BN;
+  build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
+  __syncthreads();
+  const int total = s_tstart[p.n_groups];
+  const TileIter it = tile_range(total);
+  const float* A = static_cast<const float*>(p.a);
+  float* O = static_cast<float*>(p.out);
+
+  for (int tile = it.next; tile < it.end; tile += it.step) {
+    const int e = find_group(s_tstart, p.n_groups, tile);
+    const int g0 = s_goff[e], g1 = s_goff[e + 1];
+    const int mtiles = (g1 - g0 + BM - 1) / BM;
+    const int local = tile - s_tstart[e];
+    const int mt = local % mtiles, nt = local / mtiles;
+    const int row0 = g0 + mt * BM, rows = min(BM, g1 - row0), n0 = nt * BN;
+    float acc[NW][2][4] = {};
+    for (int k0 = 0; k0 < p.K; k0 += KC) {
+      for (int i = tid; i < BM * KC; i += 256) {
+        const int r = i / KC, kk = i % KC;
+        const int rr = row0 + min(r, rows - 1);
+        int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
+        src = min(max(src, 0), p.a_rows - 1);
+        sA[r][kk] = A[(size_t)src * p.K + k0 + kk];
+      }
+      for (int i = tid; i < NW * KC * BN; i += 256) {
+        const int m = i / (KC * BN), v = i % (KC * BN), kk = v / BN, n = v % BN;
+        const float* W = static_cast<const float*>(m == 0 ? p.w0 : p.w1);
+        sB[m][kk][n] = W[((size_t)e * p.K + k0 + kk) * p.N + n0 + n];
+      }
+      __syncthreads();
+      for (int kk = 0; kk < KC; ++kk) {
+        const float a0 = sA[ty][kk], a1 = sA[ty + 16][kk];
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float b = sB[m][kk][tx + 16 * c];
+            acc[m][0][c] = fmaf(a0, b, acc[m][0][c]);
+            acc[m][1][c] = fmaf(a1, b, acc[m][1][c]);
+          }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = ty + 16 * h;
+      if (row >= rows) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float v;
+        if constexpr (GU) v = silu_mul(acc[0][h][c], acc[1][h][c]);
+        else v = acc[0][h][c];
+        O[(size_t)(row0 + row) * p.N + n0 + tx + 16 * c] = v;
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool GU, bool Q4>
+hipError_t run_bf16(const GemmParams& p, int waves_per_cu, hipStream_t s) {
+  using C = Cfg<BM, BN, WM, WN, GU, Q4>;
+  const size_t lds = C::lds_bytes(p.n_groups);
+  // Upper bound of the tile count: every group adds at most one partial m-tile.
+  const long long max_tiles = ((long long)(p.rows_cap + BM - 1) / BM + p.n_groups) * (p.N / BN);
+  long long grid = (long long)device_cu_count() * waves_per_cu;
+  if (grid > max_tiles) grid = max_tiles;
+  grid = ((grid + 7) / 8) * 8;
+  if (grid < 8) grid = 8;
+  k_gemm_bf16<BM, BN, WM, WN, GU, Q4><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
+  return hipGetLastError();
+}
+
+template <bool GU>
+hipError_t run_f32(const GemmParams& p, hipStream_t s) {
+  const size_t lds = 2 * sizeof(int) * (p.n_groups + 1);
+  const long long max_tiles = ((long long)(p.rows_cap + 31) / 32 + p.n_groups) * (p.N / 64);
+  long long grid = (long long)device_cu_count() * 4;
+  if (grid > max_tiles) grid = max_tiles;
+  grid = ((grid + 7) / 8) * 8;
+  if (grid < 8) grid = 8;
+  k_gemm_f32<GU><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
+  GemmParams p;
+  p.a = a.a; p.row_index = a.row_index; p.group_offsets = a.group_offsets;
+  p.w0 = a.w0; p.w1 = a.w1; p.s0 = a.s0; p.s1 = a.s1; p.out = a.out;
+  p.K = a.K; p.N = a.N; p.n_groups = a.n_groups; p.rows_cap = a.rows_cap; p.a_rows = a.a_rows;
+  p.row_div = a.row_div; p.group_size = a.group_size > 0 ? a.group_size : a.K;
+  const bool gu = a.op == MOE_OP_GATE_UP_SWIGLU;
+  if (a.act_dtype == MOE_DT_F32) return gu ? run_f32<true>(p, s) : run_f32<false>(p, s);
+  const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
+  const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
+  if (gu) {
+    if (small_m) return q4 ? run_bf16<32, 64, 1, 4, true, true>(p, 4, s)
+                           : run_bf16<32, 64, 1, 4, true, false>(p, 4, s);
+    return q4 ? run_bf16<128, 64, 2, 2, true, true>(p, 2, s)
+              : run_bf16<128, 64, 2, 2, true, false>(p, 2, s);
+  }
+  if (small_m) return q4 ? run_bf16<32, 128, 1, 4, false, true>(p, 4, s)
+                         : run_bf16<32, 128, 1, 4, false, false>(p, 4, s);
+  return q4 ? run_bf16<128, 128, 2, 2, false, true>(p, 2, s)
+            : run_bf16<128, 128, 2, 2, false, false>(p, 2, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,129 @@
+// Softmax top-k routing and routing-blob packing for gfx950.
+//
+// Routing follows "Systems engineering playbook: optimizing Qwen 3.5-397B MoE on Ironwood
+// (TPU7x)", section 1 (sparse MoE: softmax over the experts, top-k selected), with the
+// renormalised weight sequence stated in moe.h.  The blob layout follows section 3 (3-to-2
+// all-gather: ids and weight bits stacked on a new leading axis in one int32 array).
+//
+// One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers, and
+// each of the k rounds is a lane-local scan followed by a 6-step butterfly argmax across the wave
+// (key: larger logit, then smaller expert id).  The weights need no E-term reduction: slot j's
+// weight only involves the k selected logits.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// e^d for d <= 0 from correctly rounded fp32 operations: multiply, rint, fma, and an exact
+// scaling by 2^n.  Steps and constants as declared for moe_route in moe.h.
+__device__ __forceinline__ float exp_neg(float d) {
+#pragma clang fp contract(off)
+  constexpr double kLn2 = 0.693147180559945309417232121458176568;
+  constexpr float kLog2e = (float)(1.0 / kLn2);
+  constexpr float kLn2Hi = (float)kLn2;
+  constexpr float kLn2Lo = (float)(kLn2 - (double)kLn2Hi);
+  constexpr float kC2 = (float)(1.0 / 2.0), kC3 = (float)(1.0 / 6.0), kC4 = (float)(1.0 / 24.0);
+  constexpr float kC5 = (float)(1.0 / 120.0), kC6 = (float)(1.0 / 720.0);
+  constexpr float kC7 = (float)(1.0 / 5040.0);
+  if (d < -86.0f) return 0.0f;
+  const float n = __builtin_rintf(d * kLog2e);            // in [-124, 0]
+  float r = __builtin_fmaf(-n, kLn2Hi, d);
+  r = __builtin_fmaf(-n, kLn2Lo, r);
+  float p = kC7;
+  p = __builtin_fmaf(p, r, kC6);
+  p = __builtin_fmaf(p, r, kC5);
+  p = __builtin_fmaf(p, r, kC4);
+  p = __builtin_fmaf(p, r, kC3);
+  p = __builtin_fmaf(p, r, kC2);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const float two_n = __uint_as_float((uint32_t)((int)n + 127) << 23);  // 2^n, a normal number
+  return p * two_n;                                        // exact: the product stays normal
+}
+
+constexpr int kNone = 0x7fffffff;
+
+// (v, id) beats (bv, bid): larger logit, or equal logit (-0 == +0) and smaller id.
+__device__ __forceinline__ bool beats(float v, int id, float bv, int bid) {
+  if (id == kNone) return false;
+  if (bid == kNone) return true;
+  return v > bv || (v == bv && id < bid);
+}
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ w) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                     // uniform per wave
+  const float* row = logits + (size_t)t * E;
+  float v[PER_LANE];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = 0.0f;
+    if (e < E) { v[i] = __builtin_nontemporal_load(row + e); avail |= 1u << i; }
+  }
+  float sel_v = 0.0f;   // slot `lane` (lanes < k)
+  int sel_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int bid = kNone;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i)
+      if ((avail >> i) & 1u) {
+        const int e = lane + 64 * i;
+        if (beats(v[i], e, bv, bid)) { bv = v[i]; bid = e; }
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oid = __shfl_xor(bid, off);
+      if (beats(ov, oid, bv, bid)) { bv = ov; bid = oid; }
+    }
+    if (lane == (bid & 63)) avail &= ~(1u << (bid >> 6));
+    if (lane == j) { sel_v = bv; sel_id = bid; }
+  }
+  const float m = __shfl(sel_v, 0);
+  const float e = (lane < k) ? exp_neg(sel_v - m) : 0.0f;
+  float s = __shfl(e, 0);
+  for (int j = 1; j < k; ++j) s = s + __shfl(e, j);      // left to right
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = sel_id;
+    w[(size_t)t * k + lane] = e / s;                     // correctly rounded division
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pack(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                              int64_t P, int32_t* __restrict__ blob) {
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < P;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    blob[p] = ids[p];
+    blob[P + p] = __float_as_int(w[p]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64) k_route<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 128) k_route<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 256) k_route<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 512) k_route<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else k_route<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const int32_t* ids, const float* w, int T, int k, int32_t* blob, hipStream_t s) {
+  const int64_t P = (int64_t)T * k;
+  int64_t blocks = (P + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  k_pack<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(ids, w, P, blob);
+  return hipGetLastError();
+}
+
+}  // namespace moe

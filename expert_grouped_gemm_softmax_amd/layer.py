@@ -1,0 +1,158 @@
+"""One device's share of a routed MoE feed-forward layer, composed from the C ABI's five calls:
+route -> pack_routing -> permute -> grouped_gemm(gate/up + SwiGLU) -> grouped_gemm(down)
+[-> shared expert] -> combine.  Buffers are allocated once per token count and reused."""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _abi, ops
+
+
+@dataclass
+class ExpertWeights:
+    """Device-resident weights of the local experts (and of the optional shared expert).
+
+    Dense: w_gate, w_up [e_local][H][I], w_down [e_local][I][H] in the activation dtype.
+    int4:  int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N].
+    Shared expert (dense, activation dtype): gate, up [H][Is], down [Is][H]."""
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    s_gate: torch.Tensor | None = None
+    s_up: torch.Tensor | None = None
+    s_down: torch.Tensor | None = None
+    group_size: int = 0
+    shared_gate: torch.Tensor | None = None
+    shared_up: torch.Tensor | None = None
+    shared_down: torch.Tensor | None = None
+
+    @property
+    def int4(self) -> bool:
+        return self.w_gate.dtype == torch.int32
+
+
+def _t(a: np.ndarray, device) -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def upload(inputs: dict, cfg, device="cuda") -> tuple[torch.Tensor, torch.Tensor, ExpertWeights]:
+    """Copy a workloads.make_inputs() dict to the GPU -> (x, logits, weights)."""
+    x = _t(inputs["x"], device)
+    logits = _t(inputs["logits"], device)
+    kw = dict(w_gate=_t(inputs["w_gate"], device), w_up=_t(inputs["w_up"], device),
+              w_down=_t(inputs["w_down"], device))
+    if cfg.wfmt == "int4":
+        kw.update(s_gate=_t(inputs["w_gate_scale"], device), s_up=_t(inputs["w_up_scale"], device),
+                  s_down=_t(inputs["w_down_scale"], device), group_size=cfg.group_size)
+    if cfg.shared_I:
+        kw.update(shared_gate=_t(inputs["shared_gate"], device), shared_up=_t(inputs["shared_up"], device),
+                  shared_down=_t(inputs["shared_down"], device))
+    return x, logits, ExpertWeights(**kw)
+
+
+@dataclass
+class Buffers:
+    ids: torch.Tensor
+    w: torch.Tensor
+    blob: torch.Tensor
+    sorted_pairs: torch.Tensor
+    group_offsets: torch.Tensor
+    pair_pos: torch.Tensor
+    h: torch.Tensor
+    o: torch.Tensor
+    y: torch.Tensor
+    shared_offsets: torch.Tensor | None = None
+    shared_h: torch.Tensor | None = None
+    shared_o: torch.Tensor | None = None
+    extra: dict = field(default_factory=dict)
+
+
+class MoELayer:
+    """Routed MoE layer over local experts [e_first, e_first + e_local) of E global experts."""
+
+    def __init__(self, H: int, I: int, E: int, k: int, e_first: int, e_local: int,
+                 weights: ExpertWeights, act_dtype=torch.bfloat16, y_dtype=None):
+        self.H, self.I, self.E, self.k = H, I, E, k
+        self.e_first, self.e_local = e_first, e_local
+        self.weights = weights
+        self.act_dtype = act_dtype
+        self.y_dtype = y_dtype or act_dtype
+        self.shared_I = 0 if weights.shared_gate is None else weights.shared_gate.shape[1]
+        self._buf: dict[int, Buffers] = {}
+
+    @classmethod
+    def from_config(cls, cfg, weights: ExpertWeights, y_dtype=None):
+        act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+        return cls(cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_first, cfg.e_local, weights, act, y_dtype)
+
+    def rows_capacity(self, T: int) -> int:
+        return T * min(self.k, self.e_local)
+
+    def buffers(self, T: int, device) -> Buffers:
+        b = self._buf.get(T)
+        if b is None:
+            k, cap = self.k, self.rows_capacity(T)
+            i32 = dict(dtype=torch.int32, device=device)
+            act = dict(dtype=self.act_dtype, device=device)
+            b = Buffers(ids=torch.empty((T, k), **i32), w=torch.empty((T, k), dtype=torch.float32, device=device),
+                        blob=torch.empty((2, T, k), **i32), sorted_pairs=torch.empty(T * k, **i32),
+                        group_offsets=torch.empty(self.e_local + 1, **i32), pair_pos=torch.empty(T * k, **i32),
+                        h=torch.empty((cap, self.I), **act), o=torch.empty((cap, self.H), **act),
+                        y=torch.empty((T, self.H), dtype=self.y_dtype, device=device))
+            if self.shared_I:
+                b.shared_offsets = torch.tensor([0, T], **i32)
+                b.shared_h = torch.empty((T, self.shared_I), **act)
+                b.shared_o = torch.empty((T, self.H), **act)
+            self._buf[T] = b
+        return b
+
+    def m_hint(self, T: int) -> int:
+        return max(1, -(-T * self.k // self.E))
+
+    # -- the steps, individually callable (the benchmark times them one by one) -----------------
+    def step_route(self, logits, b, stream=None):
+        ops.route(logits, self.k, b.ids, b.w, stream=stream)
+        ops.pack_routing(b.ids, b.w, b.blob, stream=stream)
+        ops.permute(b.blob, self.e_first, self.e_local, b.sorted_pairs, b.group_offsets, b.pair_pos,
+                    stream=stream)
+
+    def step_gate_up(self, x, b, stream=None):
+        W = self.weights
+        ops.grouped_gemm(_abi.MOE_OP_GATE_UP_SWIGLU, x, b.group_offsets, W.w_gate, W.w_up, b.h,
+                         K=self.H, N=self.I, row_index=b.sorted_pairs, row_div=self.k, s0=W.s_gate,
+                         s1=W.s_up, group_size=W.group_size, m_hint=self.m_hint(x.shape[0]), stream=stream)
+
+    def step_down(self, x, b, stream=None):
+        W = self.weights
+        ops.grouped_gemm(_abi.MOE_OP_DOWN, b.h, b.group_offsets, W.w_down, None, b.o, K=self.I, N=self.H,
+                         s0=W.s_down, group_size=W.group_size, m_hint=self.m_hint(x.shape[0]), stream=stream)
+
+    def step_shared(self, x, b, stream=None):
+        W, T = self.weights, x.shape[0]
+        ops.grouped_gemm(_abi.MOE_OP_GATE_UP_SWIGLU, x, b.shared_offsets, W.shared_gate, W.shared_up,
+                         b.shared_h, K=self.H, N=self.shared_I, m_hint=T, stream=stream)
+        ops.grouped_gemm(_abi.MOE_OP_DOWN, b.shared_h, b.shared_offsets, W.shared_down, None, b.shared_o,
+                         K=self.shared_I, N=self.H, m_hint=T, stream=stream)
+
+    def step_combine(self, b, stream=None):
+        ops.combine(b.o, b.blob, b.pair_pos, b.shared_o if self.shared_I else None, b.y, stream=stream)
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, stream=None) -> torch.Tensor:
+        """x [T][H] (activation dtype), logits fp32 [T][E] -> y [T][H] (y dtype).  The returned
+        tensor is this layer's buffer for T tokens and is overwritten by the next call."""
+        T = x.shape[0]
+        assert x.dtype == self.act_dtype and tuple(logits.shape) == (T, self.E)
+        b = self.buffers(T, x.device)
+        self.step_route(logits, b, stream)
+        self.step_gate_up(x, b, stream)
+        self.step_down(x, b, stream)
+        if self.shared_I:
+            self.step_shared(x, b, stream)
+        self.step_combine(b, stream)
+        return b.y

@@ -1,0 +1,113 @@
+"""The five entry points of the C ABI on torch tensors.
+
+PyTorch is used only for device memory and the current stream: each function checks shapes,
+dtypes and devices, then passes raw pointers to libmoe_mi355x.so.  Every step of the layer runs
+in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import check, load
+
+_DT = {torch.float32: _abi.MOE_DT_F32, torch.bfloat16: _abi.MOE_DT_BF16}
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("expected a GPU tensor")
+            if not t.is_contiguous():
+                raise ValueError("expected a contiguous tensor")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def route(logits: torch.Tensor, k: int, ids: torch.Tensor | None = None, w: torch.Tensor | None = None,
+          stream=None):
+    """Softmax top-k routing of fp32 logits [T][E] -> (ids int32 [T][k], w fp32 [T][k])."""
+    T, E = logits.shape
+    assert logits.dtype == torch.float32
+    ids = ids if ids is not None else torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = w if w is not None else torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _dev(logits, ids, w)
+    check("moe_route", load().moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
+
+
+def pack_routing(ids: torch.Tensor, w: torch.Tensor, blob: torch.Tensor | None = None, stream=None):
+    """ids int32 [T][k], w fp32 [T][k] -> blob int32 [2][T][k]."""
+    T, k = ids.shape
+    assert ids.dtype == torch.int32 and w.dtype == torch.float32 and w.shape == ids.shape
+    blob = blob if blob is not None else torch.empty((2, T, k), dtype=torch.int32, device=ids.device)
+    _dev(ids, w, blob)
+    check("moe_pack_routing", load().moe_pack_routing(_ptr(ids), _ptr(w), T, k, _ptr(blob), _stream(stream)))
+    return blob
+
+
+def permute(blob: torch.Tensor, e_first: int, e_local: int, sorted_pairs=None, group_offsets=None,
+            pair_pos=None, stream=None):
+    """blob [2][T][k] -> (sorted_pairs [T*k], group_offsets [e_local+1], pair_pos [T*k])."""
+    _, T, k = blob.shape
+    assert blob.dtype == torch.int32
+    dev = blob.device
+    sp = sorted_pairs if sorted_pairs is not None else torch.empty(T * k, dtype=torch.int32, device=dev)
+    off = group_offsets if group_offsets is not None else torch.empty(e_local + 1, dtype=torch.int32, device=dev)
+    pp = pair_pos if pair_pos is not None else torch.empty(T * k, dtype=torch.int32, device=dev)
+    _dev(blob, sp, off, pp)
+    check("moe_permute", load().moe_permute(_ptr(blob), T, k, e_first, e_local, _ptr(sp), _ptr(off),
+                                            _ptr(pp), _stream(stream)))
+    return sp, off, pp
+
+
+def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torch.Tensor,
+                 w1: torch.Tensor | None, out: torch.Tensor, *, K: int, N: int, row_index=None,
+                 row_div: int = 1, s0=None, s1=None, group_size: int = 0, m_hint: int = 0, stream=None):
+    """One grouped GEMM (see moe_grouped_gemm in include/moe.h).  Weights are dense
+    [n_groups][K][N] in the activation dtype, or int32 int4 words [n_groups][K/8][N] with bf16
+    scales s0/s1 [n_groups][K/group_size][N]."""
+    _dev(a, group_offsets, w0, w1, out, row_index, s0, s1)
+    args = _abi.MoeGemmArgs()
+    args.op = op
+    args.act_dtype = _DT[a.dtype]
+    args.wfmt = _abi.MOE_W_INT4_SYM_GROUP if w0.dtype == torch.int32 else _abi.MOE_W_DENSE
+    args.group_size = group_size if args.wfmt == _abi.MOE_W_INT4_SYM_GROUP else 0
+    args.K, args.N = K, N
+    args.n_groups = group_offsets.numel() - 1
+    args.rows_cap = out.shape[0]
+    args.a_rows = a.shape[0]
+    args.row_div = row_div
+    args.m_hint = m_hint
+    args.reserved = 0
+    assert out.dtype == a.dtype and a.shape[1] == K and out.shape[1] == N
+    args.a, args.row_index, args.group_offsets = _ptr(a), _ptr(row_index), _ptr(group_offsets)
+    args.w0, args.w1, args.s0, args.s1, args.out = _ptr(w0), _ptr(w1), _ptr(s0), _ptr(s1), _ptr(out)
+    check("moe_grouped_gemm", load().moe_grouped_gemm(ctypes.byref(args), _stream(stream)))
+    return out
+
+
+def combine(expert_out: torch.Tensor, blob: torch.Tensor, pair_pos: torch.Tensor, shared_out=None,
+            y: torch.Tensor | None = None, y_dtype=None, stream=None):
+    """-> y [T][H]: sum over each token's local slots of w * expert_out[row] (+ shared_out)."""
+    _, T, k = blob.shape
+    H = expert_out.shape[1]
+    y_dtype = y_dtype or expert_out.dtype
+    y = y if y is not None else torch.empty((T, H), dtype=y_dtype, device=expert_out.device)
+    _dev(expert_out, blob, pair_pos, shared_out, y)
+    if shared_out is not None:
+        assert shared_out.dtype == expert_out.dtype and tuple(shared_out.shape) == (T, H)
+    check("moe_combine", load().moe_combine(_ptr(expert_out), expert_out.shape[0], _DT[expert_out.dtype],
+                                            _ptr(blob), _ptr(pair_pos), _ptr(shared_out), T, k, H, _ptr(y),
+                                            _DT[y.dtype], _stream(stream)))
+    return y

@@ -1,0 +1,180 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: one device's share of a routed sparse mixture-of-experts
+ * feed-forward layer on AMD MI355X (gfx950).
+ *
+ * The layer (as stated in "Systems engineering playbook: optimizing Qwen 3.5-397B MoE on Ironwood
+ * (TPU7x)", sections 1 and 3, and "vLLM TPU Inference v0.31.0", 4-bit weight scope):
+ *   1. moe_route         softmax top-k routing of each token over E experts, renormalised weights;
+ *   2. moe_pack_routing  ids and weight bits packed into one int32 routing blob;
+ *   3. moe_permute       the pairs routed to this device's experts, grouped expert by expert;
+ *   4. moe_grouped_gemm  per-expert SwiGLU FFN: fused gate/up projection + SwiGLU, then the down
+ *                        projection, with bf16 or symmetric int4 group-quantised (W4A16) weights;
+ *   5. moe_combine       weighted sum of each token's expert outputs back in token order.
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is a DEVICE pointer owned by the caller.  The library never allocates,
+ *     frees or synchronises; each call only enqueues kernels on `stream` (a hipStream_t; NULL is
+ *     the null stream) and returns.  Results are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before anything is enqueued; an invalid call returns
+ *     MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED and enqueues nothing.  A failed launch returns
+ *     MOE_ERR_HIP.  Validation needs no GPU.
+ *   - Data-dependent preconditions are not checked on the device: logits are finite, blob ids are
+ *     in [0, E).  Kernels clamp every index they read, so violating them gives wrong values, not
+ *     out-of-bounds accesses.
+ *   - Row-major layouts; "bf16" is IEEE bfloat16 stored in 16 bits; conversions to bf16 round to
+ *     nearest even.  No call depends on the number of local pairs being known on the host.
+ *   - The library's only global state is a per-device cache of the compute-unit count; calls on
+ *     different streams may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, size out of range, inconsistent sizes */
+  MOE_ERR_UNSUPPORTED = 2,   /* well-formed request outside what the library implements */
+  MOE_ERR_HIP = 3            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+/* Expert weight formats.  MOE_W_INT4_SYM_GROUP: symmetric int4 with one bf16 scale per group of
+ * `group_size` consecutive K rows per output column ("vLLM TPU Inference v0.31.0", 4-bit weight
+ * scope: symmetric int4, group-wise scales, activations not quantised; asymmetric, 8-bit and
+ * activation-order variants are not supported there and are not representable here).
+ * Layout for a [K][N] matrix of expert e: words int32 [E][K/8][N], the two's-complement nibble at
+ * bits 4i..4i+3 of word [e][kb][n] is q[8*kb+i][n]; scales bf16 [E][K/group_size][N];
+ * weight = q * scale.  Channel-wise scales are group_size == K. */
+typedef enum moe_wfmt { MOE_W_DENSE = 0, MOE_W_INT4_SYM_GROUP = 1 } moe_wfmt;
+
+typedef enum moe_gemm_op {
+  MOE_OP_GATE_UP_SWIGLU = 0,  /* out = silu(A Wg) * (A Wu), silu(z) = z / (1 + e^-z) */
+  MOE_OP_DOWN = 1             /* out = A Wd */
+} moe_gemm_op;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION at build time). */
+int moe_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_string(int status);
+
+/*
+ * moe_route -- softmax top-k routing ("Systems engineering playbook ...", section 1, sparse MoE:
+ * the router projects the token and picks the top experts of a softmax over all experts).
+ *   logits    fp32 [T][E]   router logits (finite).
+ *   topk_ids  int32 [T][k]  out: global expert ids, slot order by descending logit, ties to the
+ *                           lower expert id (-0 equals +0).
+ *   topk_w    fp32 [T][k]   out: weights renormalised over the k selected experts, evaluated as
+ *                           m = logit of slot 0, e_j = exp_ref(l_j - m), S = e_0 + e_1 + ... (left to
+ *                           right), w_j = e_j / S with correctly rounded fp32 operations and no
+ *                           contraction; exp_ref(d) = p(r) * 2^n with n = rint(d * fl(log2 e)),
+ *                           r = d - n*ln2 (two fma with the fp32 high and low parts of ln 2),
+ *                           p = degree-7 Taylor polynomial with fp32 coefficients 1/i! in Horner
+ *                           form (fma), and 0 for d < -86.  Equal in exact arithmetic to a softmax
+ *                           over all E experts restricted to the selected ones and renormalised.
+ *   Limits: 1 <= T, 1 <= E <= 1024, 1 <= k <= min(E, 64); T * E < 2^31.
+ */
+moe_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                     void* stream);
+
+/*
+ * moe_pack_routing -- routing blob ("Systems engineering playbook ...", section 3, 3-to-2
+ * all-gather: ids and weights share their shape, are stacked on a new axis, bitcast and packed
+ * into one dense int32 array, to be unpacked locally after one collective).
+ *   blob int32 [2][T][k] out: blob[0][t][j] = topk_ids[t][j]; blob[1][t][j] = bits of topk_w[t][j].
+ *   Limits: 1 <= T, 1 <= k <= 64, T * k < 2^31.
+ */
+moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T, int k,
+                            int32_t* blob, void* stream);
+
+/*
+ * moe_permute -- keep the pairs routed to this device's experts and group them by expert
+ * ("Systems engineering playbook ...", section 3, option B: each device filters and computes only
+ * the inputs of its local experts).  Pair p = t*k + j is local iff
+ * e_first <= blob[0][t][j] < e_first + e_local.
+ *   sorted_pairs  int32 [T*k]        out: rows [0, n_loc) hold the local pairs grouped by local
+ *                                    expert, ascending p within a group (stable counting sort);
+ *                                    rows >= n_loc are left untouched.
+ *   group_offsets int32 [e_local+1]  out: group e owns rows [off[e], off[e+1]); off[0] = 0,
+ *                                    off[e_local] = n_loc.
+ *   pair_pos      int32 [T*k]        out: row of pair p in sorted_pairs, or -1 if p is not local.
+ *   Limits: 1 <= T, 1 <= k <= 64, 1 <= e_local <= 1024, e_first >= 0, T * k < 2^31.
+ *   Deterministic: the output does not depend on scheduling.
+ */
+moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
+                       int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
+                       void* stream);
+
+/*
+ * moe_grouped_gemm -- one grouped GEMM over the experts of this device ("Systems engineering
+ * playbook ...", executive summary: the grouped GEMM building block; section 1: experts of
+ * intermediate size 1024, read here as SwiGLU FFNs without biases; "vLLM TPU Inference v0.31.0",
+ * 4-bit weight scope: int4 weights stay packed in HBM and only the tiles in use are dequantised on
+ * chip).  Group e covers output rows [group_offsets[e], group_offsets[e+1]); output row r uses
+ * A row a[row_index[r] / row_div] (or a[r] when row_index is NULL) and expert e's weights.
+ * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg[e][k][n]) * (sum_k A[k] Wu[e][k][n]).
+ * DOWN:           out[r][n] = sum_k A[k] Wd[e][k][n].
+ * bf16 path: bf16 operands, fp32 accumulation, bf16 output (int4 weights are dequantised to bf16
+ * in LDS).  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are not written.
+ */
+typedef struct moe_gemm_args {
+  int32_t op;          /* moe_gemm_op */
+  int32_t act_dtype;   /* moe_dtype of a, out and dense weights */
+  int32_t wfmt;        /* moe_wfmt of w0 / w1 (int4 requires MOE_DT_BF16) */
+  int32_t group_size;  /* int4: K rows per scale; a multiple of 64 that divides K.  Dense: 0 */
+  int32_t K;           /* contraction length: H for GATE_UP, I for DOWN; multiple of 64 */
+  int32_t N;           /* output columns: I for GATE_UP (multiple of 64), H for DOWN (multiple
+                          of 128) */
+  int32_t n_groups;    /* experts in this call, 1..1024 */
+  int32_t rows_cap;    /* rows of out; group_offsets[n_groups] <= rows_cap */
+  int32_t a_rows;      /* rows of a (tokens for GATE_UP, rows_cap for DOWN) */
+  int32_t row_div;     /* >= 1; divisor applied to row_index (k for GATE_UP after moe_permute) */
+  int32_t m_hint;      /* expected rows per group, a launch-shape hint only (0: unknown) */
+  int32_t reserved;    /* must be 0 */
+  const void* a;                 /* [a_rows][K] act dtype */
+  const int32_t* row_index;      /* [rows_cap] (e.g. sorted_pairs) or NULL for identity rows */
+  const int32_t* group_offsets;  /* [n_groups+1] non-decreasing, [0] = 0 (e.g. from moe_permute) */
+  const void* w0;      /* GATE_UP: Wg; DOWN: Wd.  Dense [n_groups][K][N]; int4 words [n_groups][K/8][N] */
+  const void* w1;      /* GATE_UP: Wu (same layout as w0); DOWN: NULL */
+  const void* s0;      /* int4: bf16 scales of w0 [n_groups][K/group_size][N]; dense: NULL */
+  const void* s1;      /* int4: bf16 scales of w1; otherwise NULL */
+  void* out;           /* [rows_cap][N] act dtype */
+} moe_gemm_args;
+
+moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
+
+/*
+ * moe_combine -- weighted sum back to token order ("Systems engineering playbook ...",
+ * executive summary: the unpermute building block; section 1: the always-executed shared expert
+ * is added to the routed output, its formula being read as plain addition).
+ *   expert_out  [expert_rows][H] act dtype   rows indexed by pair_pos (e.g. the DOWN output).
+ *   blob        int32 [2][T][k]              weights are read from plane 1.
+ *   pair_pos    int32 [T*k]                  from moe_permute; -1 (or any value outside
+ *                                            [0, expert_rows)) marks a pair without a row.
+ *   shared_out  [T][H] act dtype or NULL.
+ *   y           [T][H] y_dtype               out: y[t] = sum_{j ascending, valid pair_pos}
+ *                                            w[t][j] * expert_out[pair_pos[t*k+j]]
+ *                                            (+ shared_out[t]), accumulated in fp32 in that
+ *                                            order (deterministic, no atomics); a token with no
+ *                                            local pair gets 0 (+ shared_out[t]).
+ *   Limits: 1 <= T, 1 <= k <= 64, H a multiple of 8, 1 <= expert_rows, T * k < 2^31; act_dtype
+ *   and y_dtype in {MOE_DT_F32, MOE_DT_BF16}.
+ */
+moe_status moe_combine(const void* expert_out, int expert_rows, int act_dtype, const int32_t* blob,
+                       const int32_t* pair_pos, const void* shared_out, int T, int k, int H,
+                       void* y, int y_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/moe.h declares, and
+rejects invalid arguments before any HIP call (so nothing here needs a GPU)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from expert_grouped_gemm_softmax_amd import _abi
+from expert_grouped_gemm_softmax_amd._abi import MoeGemmArgs
+
+INV, UNS = _abi.MOE_ERR_INVALID_ARG, _abi.MOE_ERR_UNSUPPORTED
+FAKE = 0x1000  # never dereferenced: validation rejects these calls first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built (run __graft_entry__.build())")
+    return _abi.load()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _abi.header_functions()
+    assert set(declared) >= {"moe_route", "moe_pack_routing", "moe_permute", "moe_grouped_gemm",
+                             "moe_combine", "moe_status_string", "moe_abi_version"}
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+    # only the C ABI is exported
+    assert {s for s in exported if not s.startswith("moe_")} <= {"_init", "_fini"}
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    for s in range(4):
+        assert L.moe_status_string(s)
+    assert L.moe_status_string(99) == b"unknown status"
+
+
+def test_gfx950_code_object_only():
+    import re
+    with open(_abi.LIB_PATH, "rb") as f:
+        data = f.read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-f]+)", data))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_route_validation(L):
+    ok = (FAKE, 8, 16, 2, FAKE, FAKE, None)
+    bad = [
+        (None, 8, 16, 2, FAKE, FAKE, None), (FAKE, 8, 16, 2, None, FAKE, None),
+        (FAKE, 8, 16, 2, FAKE, None, None), (FAKE, 0, 16, 2, FAKE, FAKE, None),
+        (FAKE, 8, 0, 1, FAKE, FAKE, None), (FAKE, 8, 1025, 2, FAKE, FAKE, None),
+        (FAKE, 8, 16, 0, FAKE, FAKE, None), (FAKE, 8, 16, 17, FAKE, FAKE, None),
+        (FAKE, 8, 512, 65, FAKE, FAKE, None), (FAKE, 1 << 22, 1024, 2, FAKE, FAKE, None),
+    ]
+    for args in bad:
+        assert L.moe_route(*args) == INV, args
+    assert ok  # the valid form would launch; not called without a GPU
+
+
+def test_pack_and_permute_validation(L):
+    assert L.moe_pack_routing(None, FAKE, 4, 2, FAKE, None) == INV
+    assert L.moe_pack_routing(FAKE, FAKE, 4, 65, FAKE, None) == INV
+    assert L.moe_pack_routing(FAKE, FAKE, 0, 2, FAKE, None) == INV
+    assert L.moe_pack_routing(FAKE, FAKE, 1 << 26, 64, FAKE, None) == INV
+    assert L.moe_permute(None, 4, 2, 0, 8, FAKE, FAKE, FAKE, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, None, FAKE, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 0, FAKE, FAKE, FAKE, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 1025, FAKE, FAKE, FAKE, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, -1, 8, FAKE, FAKE, FAKE, None) == INV
+    assert L.moe_permute(FAKE, 4, 0, 0, 8, FAKE, FAKE, FAKE, None) == INV
+
+
+def _gemm(**kw):
+    a = MoeGemmArgs()
+    base = dict(op=0, act_dtype=1, wfmt=0, group_size=0, K=256, N=128, n_groups=8, rows_cap=64,
+                a_rows=32, row_div=2, m_hint=0, reserved=0, a=FAKE, row_index=FAKE, group_offsets=FAKE,
+                w0=FAKE, w1=FAKE, s0=None, s1=None, out=FAKE)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=2), INV), (dict(act_dtype=7), UNS), (dict(wfmt=5), UNS), (dict(reserved=1), INV),
+    (dict(a=None), INV), (dict(group_offsets=None), INV), (dict(w0=None), INV), (dict(out=None), INV),
+    (dict(w1=None), INV), (dict(op=1, K=128, N=256, w1=FAKE), INV), (dict(K=32), INV), (dict(K=96), INV),
+    (dict(N=32), INV), (dict(N=96), INV), (dict(op=1, K=128, N=192, w1=None), INV),
+    (dict(n_groups=0), INV), (dict(n_groups=1025), INV), (dict(rows_cap=0), INV), (dict(a_rows=0), INV),
+    (dict(row_div=0), INV), (dict(m_hint=-1), INV), (dict(row_index=None, a_rows=10), INV),
+    (dict(wfmt=1, act_dtype=0, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, group_size=32, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, group_size=96, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, K=192, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, group_size=128, s0=None, s1=FAKE), INV),
+    (dict(wfmt=1, group_size=128, s0=FAKE, s1=None), INV),
+    (dict(group_size=128), INV), (dict(s0=FAKE), INV),
+])
+def test_grouped_gemm_validation(L, kw, code):
+    assert L.moe_grouped_gemm(ctypes.byref(_gemm(**kw)), None) == code
+    assert L.moe_grouped_gemm(None, None) == INV
+
+
+def test_combine_validation(L):
+    ok = [FAKE, 64, 1, FAKE, FAKE, None, 8, 2, 256, FAKE, 1, None]
+    for i, v in [(0, None), (1, 0), (3, None), (4, None), (6, 0), (7, 0), (7, 65), (8, 0), (8, 12),
+                 (9, None)]:
+        args = list(ok)
+        args[i] = v
+        assert L.moe_combine(*args) == INV, (i, v)
+    for i, v in [(2, 3), (10, 9)]:
+        args = list(ok)
+        args[i] = v
+        assert L.moe_combine(*args) == UNS, (i, v)
