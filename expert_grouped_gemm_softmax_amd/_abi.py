@@ -16,7 +16,7 @@ MOE_OP_GATE_UP_SWIGLU, MOE_OP_DOWN = 0, 1
 class MoeGemmArgs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("op", "act_dtype", "wfmt", "group_size", "K", "N", "n_groups", "rows_cap", "a_rows",
-                 "row_div", "m_hint", "reserved")] + \
+                 "row_div", "m_hint", "out_dtype")] + \
                [(n, ctypes.c_void_p) for n in
                 ("a", "row_index", "group_offsets", "w0", "w1", "s0", "s1", "out")]
 
@@ -52,7 +52,9 @@ def load(path: str = LIB_PATH):
     L.moe_status_string.argtypes, L.moe_status_string.restype = [i32], ctypes.c_char_p
     L.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.moe_pack_routing.argtypes = [vp, vp, i32, i32, vp, vp]
-    L.moe_permute.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_permute.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), vp]
     L.moe_combine.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp]
     for fn in ("moe_route", "moe_pack_routing", "moe_permute", "moe_grouped_gemm", "moe_combine"):

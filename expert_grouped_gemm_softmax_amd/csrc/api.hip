@@ -60,15 +60,21 @@ MOE_API moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w
   return from_hip(moe::launch_pack(topk_ids, topk_w, T, k, blob, as_stream(stream)));
 }
 
+MOE_API size_t moe_permute_workspace_bytes(int T, int k, int e_local) {
+  if (T < 1 || k < 1 || k > 64 || e_local < 1 || e_local > 1024 || !fits_i32((long long)T * k)) return 0;
+  return moe::permute_workspace_bytes(T, k, e_local);
+}
+
 MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
                                int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
-                               void* stream) {
-  if (!blob || !sorted_pairs || !group_offsets || !pair_pos) return MOE_ERR_INVALID_ARG;
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!blob || !sorted_pairs || !group_offsets || !pair_pos || !workspace) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
   if (e_local < 1 || e_local > 1024 || e_first < 0 || !fits_i32((long long)e_first + e_local))
     return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe::permute_workspace_bytes(T, k, e_local)) return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_permute(blob, T, k, e_first, e_local, sorted_pairs, group_offsets,
-                                      pair_pos, as_stream(stream)));
+                                      pair_pos, workspace, as_stream(stream)));
 }
 
 MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
@@ -76,8 +82,11 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (a->op != MOE_OP_GATE_UP_SWIGLU && a->op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
   if (a->act_dtype != MOE_DT_F32 && a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP) return MOE_ERR_UNSUPPORTED;
-  if (a->reserved != 0) return MOE_ERR_INVALID_ARG;
   const bool gu = a->op == MOE_OP_GATE_UP_SWIGLU;
+  if (a->out_dtype != a->act_dtype && !(a->out_dtype == MOE_DT_F32 && !gu)) {
+    if (a->out_dtype != MOE_DT_F32 && a->out_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+    return MOE_ERR_INVALID_ARG;
+  }
   if (!a->a || !a->group_offsets || !a->w0 || !a->out) return MOE_ERR_INVALID_ARG;
   if (gu ? !a->w1 : a->w1 != nullptr) return MOE_ERR_INVALID_ARG;
   if (a->K < 64 || a->K % 64 != 0 || a->N < 64) return MOE_ERR_INVALID_ARG;

@@ -40,9 +40,10 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         hipStream_t s);
 hipError_t launch_pack(const int32_t* ids, const float* w, int T, int k, int32_t* blob,
                        hipStream_t s);
+size_t permute_workspace_bytes(int T, int k, int e_local);
 hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
                           int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
-                          hipStream_t s);
+                          void* workspace, hipStream_t s);
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s);
 hipError_t launch_combine(const void* o, int act, const int32_t* blob, const int32_t* pair_pos,
                           const void* shared, int T, int k, int H, int rows, void* y,

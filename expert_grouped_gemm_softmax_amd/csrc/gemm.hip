@@ -24,6 +24,8 @@
 //  - v_mfma_f32_16x16x32_bf16 with fp32 accumulators; SwiGLU fused in the epilogue (each lane
 //    holds the gate and the up value of the same output element).
 //  - Global loads for chunk c+1 are issued before the MFMAs of chunk c (register prefetch).
+#include <cstdlib>
+
 #include "common.h"
 
 namespace moe {
@@ -102,35 +104,46 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // ---------------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool GU, bool Q4>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_>
 struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr bool GU = GU_, Q4 = Q4_;
+  static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
   static constexpr int KC = 64;                     // K chunk per LDS stage
   static constexpr int NW = GU ? 2 : 1;             // weight matrices
   static constexpr int LDK = KC + 8;                // padded LDS row (bf16 elements): 144 bytes
   static constexpr int A_ELEMS = BM * LDK;
   static constexpr int B_ELEMS = NW * BN * LDK;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;   // u16 elements
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;   // u16 elements per LDS buffer
   static constexpr int A_LOADS = BM * (KC / 8) / 256;          // 16-byte A chunks per thread
   // B units per thread: a dense R x 8 block or one 16-byte row of 4 int4 words, 32 weights each
   static constexpr int B_UNITS = NW * KC * BN / 32 / 256;
   static constexpr int R = 4;                       // dense: k-rows per transposed block
-  static constexpr int MT = BM / WM / 16;
-  static constexpr int NTL = BN / WN / 16;
+  static constexpr int MT = BM / WM / 16;           // 16-row MFMA tiles per wave
+  static constexpr int NTL = BN / WN / 16;          // 16-column MFMA tiles per wave and matrix
   static_assert(WM * WN == 4, "four waves");
   static_assert(A_LOADS >= 1 && BM * (KC / 8) % 256 == 0, "A tile split");
   static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * 256) == 0, "B tile split");
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
-  static size_t lds_bytes(int n_groups) { return STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
+  static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
 
-template <int BM, int BN, int WM, int WN, bool GU, bool Q4>
+// Registers holding one K chunk in flight: A rows and the weight units of this thread.
+template <class C>
+struct Chunk {
+  u32x4 a[C::A_LOADS];
+  u32x4 b[C::B_UNITS][C::Q4 ? 1 : C::R];
+  u32x2 s[C::B_UNITS];
+};
+
+template <class C, typename OutT>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
-  using C = Cfg<BM, BN, WM, WN, GU, Q4>;
-  constexpr int KC = C::KC, NW = C::NW, LDK = C::LDK;
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, KC = C::KC, NW = C::NW, LDK = C::LDK;
+  constexpr int MT = C::MT, NTL = C::NTL;
   extern __shared__ __attribute__((aligned(16))) u16 smem[];
-  u16* sA = smem;
-  u16* sB = smem + C::A_ELEMS;
-  int* s_tstart = reinterpret_cast<int*>(smem + C::STAGE);
+  u16* buf0 = smem;
+  u16* buf1 = smem + (C::STAGES - 1) * C::STAGE;
+  int* s_tstart = reinterpret_cast<int*>(smem + C::STAGES * C::STAGE);
   int* s_goff = s_tstart + (p.n_groups + 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -144,7 +157,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
   const TileIter it = tile_range(total);
 
   const u16* A = static_cast<const u16*>(p.a);
-  u16* O = static_cast<u16*>(p.out);
+  OutT* O = static_cast<OutT*>(p.out);
+  const int arow = wm * (BM / WM) + (lane & 15);
+  const int bcol = wn * (BN / WN) + (lane & 15);
+  const int kofs = (lane >> 4) * 8;
 
   for (int tile = it.next; tile < it.end; tile += it.step) {
     const int e = find_group(s_tstart, p.n_groups, tile);
@@ -155,29 +171,32 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     const int row0 = g0 + mt * BM;
     const int rows = min(BM, g1 - row0);
     const int n0 = nt * BN;
+    // 16-row MFMA tiles of this wave that hold at least one valid row
+    const int wrow0 = wm * (BM / WM);
+    const int mt_live = min(MT, max(0, (rows - wrow0 + 15) / 16));
 
-    // ---- per-thread global source pointers -------------------------------------------------
+    // ---- per-thread global sources -----------------------------------------------------------
     const u16* a_src[C::A_LOADS];
     int a_lds[C::A_LOADS];
+    bool a_ok[C::A_LOADS];
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int c = tid + 256 * i;
       const int r = c / (KC / 8), kc8 = c % (KC / 8);
-      const int rr = row0 + min(r, rows - 1);              // pad rows repeat a valid row
+      a_ok[i] = r < rows;                                   // padding rows are never loaded
+      const int rr = row0 + min(r, rows - 1);
       int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
       a_src[i] = A + (size_t)src * p.K + kc8 * 8;
       a_lds[i] = r * LDK + kc8 * 8;
     }
-
-    // Dense: unit = R x 8 block (R k-rows, 8 columns); int4: unit = one 16-byte row of 4 words.
     const char* b_src[C::B_UNITS];
     const u16* s_src[C::B_UNITS];
     int b_lds[C::B_UNITS];
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i) {
       const int u = tid + 256 * i;
-      if constexpr (!Q4) {
+      if constexpr (!C::Q4) {
         constexpr int per_m = (KC / C::R) * (BN / 8);
         const int m = u / per_m, v = u % per_m;
         const int nb = v % (BN / 8), kb = v / (BN / 8);
@@ -197,62 +216,61 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
       }
     }
 
-    u32x4 ra[C::A_LOADS];
-    u32x4 rb[C::B_UNITS][Q4 ? 1 : C::R];
-    u32x2 rs[C::B_UNITS];
-
-    auto load_chunk = [&](int kc) {
+    auto load_chunk = [&](int kc, Chunk<C>& ch) {
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
-        ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kc * KC);
+        if (a_ok[i]) ch.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kc * KC);
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
-        if constexpr (!Q4) {
+        if constexpr (!C::Q4) {
 #pragma unroll
           for (int r = 0; r < C::R; ++r)
-            rb[i][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            ch.b[i][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
                 b_src[i] + ((size_t)kc * KC + r) * p.N * sizeof(u16)));
         } else {
-          rb[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          ch.b[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
               b_src[i] + (size_t)kc * (KC / 8) * p.N * sizeof(int32_t)));
           const int grp = (kc * KC) / p.group_size;
-          rs[i] = *reinterpret_cast<const u32x2*>(s_src[i] + (size_t)grp * p.N);
+          ch.s[i] = *reinterpret_cast<const u32x2*>(s_src[i] + (size_t)grp * p.N);
         }
       }
     };
 
-    auto store_chunk = [&]() {
+    auto store_chunk = [&](const Chunk<C>& ch, u16* buf) {
+      u16* sA = buf;
+      u16* sB = buf + C::A_ELEMS;
 #pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + a_lds[i]) = ra[i];
+      for (int i = 0; i < C::A_LOADS; ++i)
+        if (a_ok[i]) *reinterpret_cast<u32x4*>(sA + a_lds[i]) = ch.a[i];
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
-        if constexpr (!Q4) {
-          // rb[i][r] = row r (k), dwords d = columns (2d, 2d+1).  Column c gets k-rows 0..3.
+        if constexpr (!C::Q4) {
+          // ch.b[i][r] = k-row r, dword d = columns (2d, 2d+1); column c gets k-rows 0..3.
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const int d = c >> 1;
             uint32_t lo, hi;
             if (c & 1) {
-              lo = pack_hi16(rb[i][0][d], rb[i][1][d]);
-              hi = pack_hi16(rb[i][2][d], rb[i][3][d]);
+              lo = pack_hi16(ch.b[i][0][d], ch.b[i][1][d]);
+              hi = pack_hi16(ch.b[i][2][d], ch.b[i][3][d]);
             } else {
-              lo = pack_lo16(rb[i][0][d], rb[i][1][d]);
-              hi = pack_lo16(rb[i][2][d], rb[i][3][d]);
+              lo = pack_lo16(ch.b[i][0][d], ch.b[i][1][d]);
+              hi = pack_lo16(ch.b[i][2][d], ch.b[i][3][d]);
             }
             *reinterpret_cast<u32x2*>(sB + b_lds[i] + c * LDK) = u32x2{lo, hi};
           }
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t word = rb[i][0][c];
-            const uint32_t sbits = (c & 1) ? (rs[i][c >> 1] >> 16) : (rs[i][c >> 1] & 0xffffu);
-            const float s = __uint_as_float(sbits << 16);
+            const uint32_t word = ch.b[i][0][c];
+            const uint32_t sbits = (c & 1) ? (ch.s[i][c >> 1] >> 16) : (ch.s[i][c >> 1] & 0xffffu);
+            const float sc = __uint_as_float(sbits << 16);
             uint32_t q[4];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
               const int q0 = ((int)(word << (28 - 8 * h))) >> 28;        // nibble 2h
               const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
-              q[h] = pack_bf16x2((float)q0 * s, (float)q1 * s);
+              q[h] = pack_bf16x2((float)q0 * sc, (float)q1 * sc);
             }
             *reinterpret_cast<u32x4*>(sB + b_lds[i] + c * LDK) = u32x4{q[0], q[1], q[2], q[3]};
           }
@@ -260,59 +278,100 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
       }
     };
 
-    f32x4 acc[NW][C::MT][C::NTL];
+    f32x4 acc[NW][MT][NTL];
 #pragma unroll
     for (int m = 0; m < NW; ++m)
 #pragma unroll
-      for (int i = 0; i < C::MT; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int arow = wm * (BM / WM) + (lane & 15);
-    const int bcol = wn * (BN / WN) + (lane & 15);
-    const int kofs = (lane >> 4) * 8;
-
-    load_chunk(0);
-    for (int kc = 0; kc < nK; ++kc) {
-      store_chunk();
-      __syncthreads();
-      if (kc + 1 < nK) load_chunk(kc + 1);
+    auto compute = [&](const u16* buf) {
+      const u16* sA = buf;
+      const u16* sB = buf + C::A_ELEMS;
 #pragma unroll
       for (int ks = 0; ks < KC; ks += 32) {
-        bf16x8 av[C::MT];
+        bf16x8 av[MT];
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
-          av[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 16) * LDK + ks + kofs);
+        for (int i = 0; i < MT; ++i)
+          if (i < mt_live) av[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 16) * LDK + ks + kofs);
 #pragma unroll
         for (int m = 0; m < NW; ++m)
 #pragma unroll
-          for (int j = 0; j < C::NTL; ++j) {
+          for (int j = 0; j < NTL; ++j) {
             const bf16x8 bv =
                 *reinterpret_cast<const bf16x8*>(sB + (m * BN + bcol + j * 16) * LDK + ks + kofs);
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
+            for (int i = 0; i < MT; ++i)
+              if (i < mt_live)
+                acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
           }
       }
+    };
+
+    // ---- K loop: loads run two chunks ahead of the MFMAs (two register sets).  With two LDS
+    // buffers one barrier per chunk suffices; with one buffer (more workgroups per CU) the
+    // buffer is refilled between two barriers.
+    Chunk<C> c0, c1;
+    load_chunk(0, c0);
+    if (nK > 1) load_chunk(1, c1);
+    if constexpr (C::STAGES == 2) {
+      store_chunk(c0, buf0);
+      if (nK > 2) load_chunk(2, c0);
       __syncthreads();
+      for (int kc = 0; kc < nK; kc += 2) {
+        compute(buf0);
+        if (kc + 1 < nK) {
+          store_chunk(c1, buf1);
+          if (kc + 3 < nK) load_chunk(kc + 3, c1);
+        }
+        __syncthreads();
+        if (kc + 1 < nK) {
+          compute(buf1);
+          if (kc + 2 < nK) {
+            store_chunk(c0, buf0);
+            if (kc + 4 < nK) load_chunk(kc + 4, c0);
+          }
+          __syncthreads();
+        }
+      }
+    } else {
+      for (int kc = 0; kc < nK; kc += 2) {
+        store_chunk(c0, buf0);
+        __syncthreads();
+        if (kc + 2 < nK) load_chunk(kc + 2, c0);
+        compute(buf0);
+        __syncthreads();
+        if (kc + 1 < nK) {
+          store_chunk(c1, buf0);
+          __syncthreads();
+          if (kc + 3 < nK) load_chunk(kc + 3, c1);
+          compute(buf0);
+          __syncthreads();
+        }
+      }
     }
 
     // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile ----------
 #pragma unroll
-    for (int i = 0; i < C::MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mt_live) break;
 #pragma unroll
-      for (int j = 0; j < C::NTL; ++j)
+      for (int j = 0; j < NTL; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+          const int row = wrow0 + i * 16 + (lane >> 4) * 4 + r;
           const int col = wn * (BN / WN) + j * 16 + (lane & 15);
           if (row < rows) {
             float v;
-            if constexpr (GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
+            if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
             else v = acc[0][i][j][r];
-            O[(size_t)(row0 + row) * p.N + n0 + col] = f32_to_bf16(v);
+            OutT* dst = O + (size_t)(row0 + row) * p.N + n0 + col;
+            if constexpr (sizeof(OutT) == 4) *dst = v;
+            else *dst = f32_to_bf16(v);
           }
         }
+    }
   }
 }
 
@@ -386,17 +445,21 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GU, bool Q4>
-hipError_t run_bf16(const GemmParams& p, int waves_per_cu, hipStream_t s) {
-  using C = Cfg<BM, BN, WM, WN, GU, Q4>;
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+template <class C, typename OutT>
+hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   const size_t lds = C::lds_bytes(p.n_groups);
   // Upper bound of the tile count: every group adds at most one partial m-tile.
-  const long long max_tiles = ((long long)(p.rows_cap + BM - 1) / BM + p.n_groups) * (p.N / BN);
-  long long grid = (long long)device_cu_count() * waves_per_cu;
+  const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
+  const int fit = (int)(kLdsPerCu / lds);              // workgroups that fit in one CU's LDS
+  if (fit < 1) return hipErrorInvalidValue;
+  if (wgs_per_cu > fit) wgs_per_cu = fit;
+  long long grid = (long long)device_cu_count() * wgs_per_cu;
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  k_gemm_bf16<BM, BN, WM, WN, GU, Q4><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
+  k_gemm_bf16<C, OutT><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
   return hipGetLastError();
 }
 
@@ -414,6 +477,38 @@ hipError_t run_f32(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Tile variants.  Decode-shaped calls (few rows per expert) stream weights with 32-row tiles and
+// many workgroups per CU; prefill-shaped calls use 128-row tiles.  MOE_GEMM_VARIANT (debug only)
+// forces one variant index for tuning sweeps.
+namespace {
+
+struct Variant {
+  int bm, bn, wgs_per_cu;
+};
+
+template <int BM, int BN, int WM, int WN, int ST>
+hipError_t run_variant(const GemmParams& p, bool gu, bool q4, bool f32out, int wgs, hipStream_t s) {
+  if (gu) {
+    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true>, u16>(p, wgs, s)
+              : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false>, u16>(p, wgs, s);
+  }
+  if constexpr (BN >= 128) {
+    if (f32out)
+      return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true>, float>(p, wgs, s)
+                : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false>, float>(p, wgs, s);
+    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true>, u16>(p, wgs, s)
+              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false>, u16>(p, wgs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+}  // namespace
+
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   GemmParams p;
   p.a = a.a; p.row_index = a.row_index; p.group_offsets = a.group_offsets;
@@ -423,17 +518,37 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool gu = a.op == MOE_OP_GATE_UP_SWIGLU;
   if (a.act_dtype == MOE_DT_F32) return gu ? run_f32<true>(p, s) : run_f32<false>(p, s);
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
+  const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  if (gu) {
-    if (small_m) return q4 ? run_bf16<32, 64, 1, 4, true, true>(p, 4, s)
-                           : run_bf16<32, 64, 1, 4, true, false>(p, 4, s);
-    return q4 ? run_bf16<128, 64, 2, 2, true, true>(p, 2, s)
-              : run_bf16<128, 64, 2, 2, true, false>(p, 2, s);
+  // variant ids (rows x columns per tile for gate/up | down, LDS buffers, workgroups per CU):
+  //   0: 32x64|32x128, 1 buffer, 4     1: 32x128|32x256, 1 buffer, 4    2: 128x64|128x128, 2, 2
+  //   3: 128x128|128x256, 2, 1         4: 64x64|64x128, 2, 3            5: 32x64|32x128, 2, 3
+  int v = small_m ? 0 : 2;
+  v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
+  const int wgs = env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0);
+  const bool n256 = p.N % 256 == 0;
+  switch (v) {
+    case 1:
+      return gu ? run_variant<32, 128, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s)
+                : (n256 ? run_variant<32, 256, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s)
+                        : run_variant<32, 128, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s));
+    case 2:
+      return gu ? run_variant<128, 64, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
+                : run_variant<128, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s);
+    case 3:
+      return gu ? run_variant<128, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 1, s)
+                : (n256 ? run_variant<128, 256, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 1, s)
+                        : run_variant<128, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 1, s));
+    case 4:
+      return gu ? run_variant<64, 64, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s)
+                : run_variant<64, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s);
+    case 5:
+      return gu ? run_variant<32, 64, 1, 4, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s)
+                : run_variant<32, 128, 1, 4, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s);
+    default:
+      return gu ? run_variant<32, 64, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s)
+                : run_variant<32, 128, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s);
   }
-  if (small_m) return q4 ? run_bf16<32, 128, 1, 4, false, true>(p, 4, s)
-                         : run_bf16<32, 128, 1, 4, false, false>(p, 4, s);
-  return q4 ? run_bf16<128, 128, 2, 2, false, true>(p, 2, s)
-            : run_bf16<128, 128, 2, 2, false, false>(p, 2, s);
 }
 
 }  // namespace moe

@@ -4,87 +4,102 @@
 // (option B): each device keeps only the token-expert pairs routed to its own experts.  They are
 // grouped by expert with a stable counting sort: histogram, exclusive prefix scan, scatter.
 //
-// One workgroup of NW wavefronts.  Wave w owns a contiguous range of pairs (a multiple of 64), so
-// the stable order inside a group is: by wave, then by 64-pair step, then by lane.  Inside a
-// step, lanes carrying the same local expert are found with one ballot per bit of the local id
-// (a match-any built from ballots); the lowest such lane updates the wave's LDS counter for that
-// expert, so no atomics are needed and the result is deterministic.
+// Two launches over chunks of kChunk consecutive pairs (one workgroup of 4 wavefronts per chunk,
+// 512 pairs per wavefront):
+//   k_perm_count    per-chunk histogram of local expert ids -> workspace counts[chunk][e];
+//   k_perm_scatter  every workgroup sums the counts of the chunks before it (its row base per
+//                   expert) and of all chunks (the group offsets), recounts its own chunk per
+//                   wavefront, and writes each local pair to its row.
+// Inside a 64-pair step, lanes carrying the same local expert are found with one ballot per bit
+// of the local id (a match-any built from ballots); the lowest such lane updates the wavefront's
+// LDS counter for that expert.  Stable order = (chunk, wavefront, step, lane) = ascending pair
+// index, with no atomics, so the result is deterministic.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kUnroll = 8;
+constexpr int kWavesPerChunk = 4;
+constexpr int kSteps = 8;                                  // 64-pair steps per wavefront
+constexpr int kWavePairs = 64 * kSteps;
+constexpr int kChunk = kWavesPerChunk * kWavePairs;        // 2048 pairs per workgroup
 
-struct Match {
-  uint64_t same;   // lanes holding the same valid local id as this lane
-  bool valid;
-};
-
-__device__ __forceinline__ Match match_local(int le, bool valid, int nbits) {
+__device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
   uint64_t same = __ballot(valid);
   for (int b = 0; b < nbits; ++b) {
     const bool bit = (le >> b) & 1;
     const uint64_t bb = __ballot(valid && bit);
     same &= bit ? bb : ~bb;
   }
-  return {same, valid};
+  return same;
 }
 
-__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ blob, int P, int e_first,
-                                                  int e_local, int nbits, int32_t* __restrict__ sorted_pairs,
-                                                  int32_t* __restrict__ group_offsets,
-                                                  int32_t* __restrict__ pair_pos) {
-  extern __shared__ int32_t lds[];
-  const int NW = blockDim.x >> 6;
-  int32_t* cnt = lds;                         // [NW][e_local]: counts, then running row bases
-  int32_t* tot = lds + NW * e_local;          // [e_local]
-  int32_t* wsum = tot + e_local;              // [16]
+// Counts of this wavefront's pairs per local expert, accumulated into mine[0..e_local).
+__device__ __forceinline__ void count_wave(const int32_t* __restrict__ blob, int beg, int end, int e_first,
+                                           int e_local, int nbits, int lane, int32_t* mine) {
+  int le[kSteps];
+#pragma unroll
+  for (int u = 0; u < kSteps; ++u) {
+    const int p = beg + 64 * u + lane;
+    le[u] = (p < end) ? blob[p] - e_first : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kSteps; ++u) {
+    const bool valid = le[u] >= 0 && le[u] < e_local;
+    const uint64_t same = match_local(le[u], valid, nbits);
+    if (valid && lane == __ffsll((unsigned long long)same) - 1) mine[le[u]] += __popcll(same);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ blob, int P, int e_first,
+                                                    int e_local, int nbits, int32_t* __restrict__ counts) {
+  extern __shared__ int32_t lds[];                         // [4][e_local]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  for (int i = threadIdx.x; i < NW * e_local; i += blockDim.x) cnt[i] = 0;
+  for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) lds[i] = 0;
   __syncthreads();
-
-  const int per = ((P + NW * 64 - 1) / (NW * 64)) * 64;
-  const int beg = min(P, wv * per), end = min(P, beg + per);
-  int32_t* mine = cnt + wv * e_local;
-
-  // Pass 1: per-wave histogram of local ids.
-  for (int base = beg; base < end; base += 64 * kUnroll) {
-    int le[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + 64 * u + lane;
-      le[u] = (p < end) ? blob[p] - e_first : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bool valid = le[u] >= 0 && le[u] < e_local;
-      const Match m = match_local(le[u], valid, nbits);
-      if (valid && lane == __ffsll((unsigned long long)m.same) - 1) mine[le[u]] += __popcll(m.same);
-    }
-  }
+  const int beg = blockIdx.x * kChunk + wv * kWavePairs;
+  count_wave(blob, beg, min(P, beg + kWavePairs), e_first, e_local, nbits, lane, lds + wv * e_local);
   __syncthreads();
-
-  // Per expert: exclusive prefix over waves, and the expert's total.
   for (int e = threadIdx.x; e < e_local; e += blockDim.x) {
-    int run = 0;
-    for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w * e_local + e];
-      cnt[w * e_local + e] = run;
-      run += c;
-    }
-    tot[e] = run;
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerChunk; ++w) c += lds[w * e_local + e];
+    counts[(size_t)blockIdx.x * e_local + e] = c;
   }
-  __syncthreads();
+}
 
-  // Exclusive scan of the totals over experts, in chunks of blockDim.x.
+__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ blob, int P, int e_first,
+                                                      int e_local, int nbits, int nchunks,
+                                                      const int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ sorted_pairs,
+                                                      int32_t* __restrict__ group_offsets,
+                                                      int32_t* __restrict__ pair_pos) {
+  extern __shared__ int32_t lds[];
+  int32_t* cnt = lds;                                      // [4][e_local] wave counts -> row bases
+  int32_t* base = lds + kWavesPerChunk * e_local;          // [e_local] chunk base per expert
+  int32_t* wsum = base + e_local;                          // [4]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int chunk = blockIdx.x;
+
+  for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int beg = chunk * kChunk + wv * kWavePairs;
+  const int end = min(P, beg + kWavePairs);
+  count_wave(blob, beg, end, e_first, e_local, nbits, lane, cnt + wv * e_local);
+
+  // Per expert: pairs in earlier chunks and in all chunks; then the offsets (scan over experts).
   int carry = 0;
   for (int c0 = 0; c0 < e_local; c0 += blockDim.x) {
     const int e = c0 + threadIdx.x;
-    const int v = (e < e_local) ? tot[e] : 0;
-    int incl = v;
+    int before = 0, total = 0;
+    if (e < e_local) {
+      for (int c = 0; c < nchunks; ++c) {
+        const int v = counts[(size_t)c * e_local + e];
+        before += (c < chunk) ? v : 0;
+        total += v;
+      }
+    }
+    int incl = total;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(incl, off);
@@ -92,65 +107,77 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ bl
     }
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    if (wv == 0) {
-      int s = (lane < NW) ? wsum[lane] : 0;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const int o = __shfl_up(s, off);
-        if (lane >= off) s += o;
-      }
-      if (lane < NW) wsum[lane] = s;                      // inclusive over waves
-    }
-    __syncthreads();
-    const int wave_base = (wv == 0) ? 0 : wsum[wv - 1];
-    const int chunk_total = wsum[NW - 1];
-    __syncthreads();                                       // wsum reused by the next chunk
+    int wave_base = 0;
+    for (int w = 0; w < wv; ++w) wave_base += wsum[w];
+    const int chunk_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     if (e < e_local) {
-      const int off = carry + wave_base + incl - v;
-      group_offsets[e] = off;
-      for (int w = 0; w < NW; ++w) cnt[w * e_local + e] += off;
+      const int off = carry + wave_base + incl - total;
+      if (chunk == 0) group_offsets[e] = off;
+      base[e] = off + before;
     }
     carry += chunk_total;
+    __syncthreads();                                       // wsum reused by the next chunk of experts
   }
-  if (threadIdx.x == 0) group_offsets[e_local] = carry;
+  if (chunk == 0 && threadIdx.x == 0) group_offsets[e_local] = carry;
+
+  // Row base of each wavefront: chunk base plus the counts of the earlier wavefronts.
+  for (int e = threadIdx.x; e < e_local; e += blockDim.x) {
+    int run = base[e];
+#pragma unroll
+    for (int w = 0; w < kWavesPerChunk; ++w) {
+      const int c = cnt[w * e_local + e];
+      cnt[w * e_local + e] = run;
+      run += c;
+    }
+  }
   __syncthreads();
 
-  // Pass 2: stable scatter.
-  for (int base = beg; base < end; base += 64 * kUnroll) {
-    int le[kUnroll];
+  int32_t* mine = cnt + wv * e_local;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int le[kSteps];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + 64 * u + lane;
-      le[u] = (p < end) ? blob[p] - e_first : -1;
-    }
+  for (int u = 0; u < kSteps; ++u) {
+    const int p = beg + 64 * u + lane;
+    le[u] = (p < end) ? blob[p] - e_first : -1;
+  }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + 64 * u + lane;
-      const bool valid = le[u] >= 0 && le[u] < e_local;
-      const Match m = match_local(le[u], valid, nbits);
-      int row = -1;
-      if (valid) row = mine[le[u]] + __popcll(m.same & below);
-      if (valid && lane == __ffsll((unsigned long long)m.same) - 1) mine[le[u]] += __popcll(m.same);
-      if (p < end) {
-        pair_pos[p] = row;
-        if (valid) sorted_pairs[row] = p;
-      }
+  for (int u = 0; u < kSteps; ++u) {
+    const int p = beg + 64 * u + lane;
+    const bool valid = le[u] >= 0 && le[u] < e_local;
+    const uint64_t same = match_local(le[u], valid, nbits);
+    int row = -1;
+    if (valid) row = mine[le[u]] + __popcll(same & below);
+    if (valid && lane == __ffsll((unsigned long long)same) - 1) mine[le[u]] += __popcll(same);
+    if (p < end) {
+      pair_pos[p] = row;
+      if (valid) sorted_pairs[row] = p;
     }
   }
 }
 
 }  // namespace
 
+size_t permute_workspace_bytes(int T, int k, int e_local) {
+  const long long P = (long long)T * k;
+  const long long nchunks = (P + kChunk - 1) / kChunk;
+  return (size_t)(nchunks * e_local * (long long)sizeof(int32_t));
+}
+
 hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
                           int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
-                          hipStream_t s) {
+                          void* workspace, hipStream_t s) {
   const int P = T * k;
-  const int NW = (e_local <= 512) ? 16 : 8;
+  const int nchunks = (P + kChunk - 1) / kChunk;
   int nbits = 1;
   while ((1 << nbits) < e_local) ++nbits;
-  const size_t lds = sizeof(int32_t) * ((size_t)NW * e_local + e_local + 16);
-  k_permute<<<dim3(1), dim3(NW * 64), lds, s>>>(blob, P, e_first, e_local, nbits, sorted_pairs,
-                                                group_offsets, pair_pos);
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  const size_t lds_count = sizeof(int32_t) * kWavesPerChunk * e_local;
+  k_perm_count<<<dim3(nchunks), dim3(256), lds_count, s>>>(blob, P, e_first, e_local, nbits, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds_scatter = sizeof(int32_t) * ((kWavesPerChunk + 1) * e_local + kWavesPerChunk);
+  k_perm_scatter<<<dim3(nchunks), dim3(256), lds_scatter, s>>>(blob, P, e_first, e_local, nbits, nchunks,
+                                                               counts, sorted_pairs, group_offsets, pair_pos);
   return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@
 // all-gather: ids and weight bits stacked on a new leading axis in one int32 array).
 //
 // One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers, and
-// each of the k rounds is a lane-local scan followed by a 6-step butterfly argmax across the wave
-// (key: larger logit, then smaller expert id).  The weights need no E-term reduction: slot j's
+// each of the k rounds is a lane-local scan, a 4-step DPP reduction inside each 16-lane row and a
+// comparison of the four row winners read with v_readlane (key: larger logit, then smaller
+// expert id).  The weights need no E-term reduction: slot j's
 // weight only involves the k selected logits.
 #include "common.h"
 
@@ -50,6 +51,16 @@ __device__ __forceinline__ bool beats(float v, int id, float bv, int bid) {
   return v > bv || (v == bv && id < bid);
 }
 
+// DPP controls (gfx9 encoding): quad permutations, reverse within 8 lanes, reverse within 16.
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& bv, int& bid) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xf, 0xf, false));
+  const int oid = __builtin_amdgcn_update_dpp(0, bid, CTRL, 0xf, 0xf, false);
+  if (beats(ov, oid, bv, bid)) { bv = ov; bid = oid; }
+}
+
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
                                                int32_t* __restrict__ ids, float* __restrict__ w) {
@@ -77,19 +88,27 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
         const int e = lane + 64 * i;
         if (beats(v[i], e, bv, bid)) { bv = v[i]; bid = e; }
       }
+    // best of each 16-lane row, in every lane of that row
+    dpp_step<kQuadXor1>(bv, bid);
+    dpp_step<kQuadXor2>(bv, bid);
+    dpp_step<kRowHalfMirror>(bv, bid);
+    dpp_step<kRowMirror>(bv, bid);
+    // best of the four rows (read as wave-uniform values)
+    float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int wid = __builtin_amdgcn_readlane(bid, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oid = __shfl_xor(bid, off);
-      if (beats(ov, oid, bv, bid)) { bv = ov; bid = oid; }
+    for (int r = 16; r < 64; r += 16) {
+      const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r));
+      const int rid = __builtin_amdgcn_readlane(bid, r);
+      if (beats(rv, rid, wv, wid)) { wv = rv; wid = rid; }
     }
-    if (lane == (bid & 63)) avail &= ~(1u << (bid >> 6));
-    if (lane == j) { sel_v = bv; sel_id = bid; }
+    if (lane == (wid & 63)) avail &= ~(1u << (wid >> 6));
+    if (lane == j) { sel_v = wv; sel_id = wid; }
   }
-  const float m = __shfl(sel_v, 0);
+  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
   const float e = (lane < k) ? exp_neg(sel_v - m) : 0.0f;
-  float s = __shfl(e, 0);
-  for (int j = 1; j < k; ++j) s = s + __shfl(e, j);      // left to right
+  float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 0));
+  for (int j = 1; j < k; ++j) s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), j));
   if (lane < k) {
     ids[(size_t)t * k + lane] = sel_id;
     w[(size_t)t * k + lane] = e / s;                     // correctly rounded division

@@ -67,6 +67,7 @@ class Buffers:
     h: torch.Tensor
     o: torch.Tensor
     y: torch.Tensor
+    workspace: torch.Tensor | None = None
     shared_offsets: torch.Tensor | None = None
     shared_h: torch.Tensor | None = None
     shared_o: torch.Tensor | None = None
@@ -77,17 +78,21 @@ class MoELayer:
     """Routed MoE layer over local experts [e_first, e_first + e_local) of E global experts."""
 
     def __init__(self, H: int, I: int, E: int, k: int, e_first: int, e_local: int,
-                 weights: ExpertWeights, act_dtype=torch.bfloat16, y_dtype=None):
+                 weights: ExpertWeights, act_dtype=torch.bfloat16, y_dtype=torch.float32):
         self.H, self.I, self.E, self.k = H, I, E, k
         self.e_first, self.e_local = e_first, e_local
         self.weights = weights
         self.act_dtype = act_dtype
-        self.y_dtype = y_dtype or act_dtype
+        # Expert outputs and the layer output are fp32: each is a partial sum (over a token's
+        # experts here, over devices in an expert-parallel reduce-scatter) and a bf16 rounding of
+        # every row would add an error proportional to |y| on top of the bf16 GEMM operands.
+        self.o_dtype = torch.float32
+        self.y_dtype = y_dtype
         self.shared_I = 0 if weights.shared_gate is None else weights.shared_gate.shape[1]
         self._buf: dict[int, Buffers] = {}
 
     @classmethod
-    def from_config(cls, cfg, weights: ExpertWeights, y_dtype=None):
+    def from_config(cls, cfg, weights: ExpertWeights, y_dtype=torch.float32):
         act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
         return cls(cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_first, cfg.e_local, weights, act, y_dtype)
 
@@ -103,12 +108,15 @@ class MoELayer:
             b = Buffers(ids=torch.empty((T, k), **i32), w=torch.empty((T, k), dtype=torch.float32, device=device),
                         blob=torch.empty((2, T, k), **i32), sorted_pairs=torch.empty(T * k, **i32),
                         group_offsets=torch.empty(self.e_local + 1, **i32), pair_pos=torch.empty(T * k, **i32),
-                        h=torch.empty((cap, self.I), **act), o=torch.empty((cap, self.H), **act),
+                        h=torch.empty((cap, self.I), **act),
+                        o=torch.empty((cap, self.H), dtype=self.o_dtype, device=device),
                         y=torch.empty((T, self.H), dtype=self.y_dtype, device=device))
+            b.workspace = torch.empty(max(1, ops.permute_workspace_bytes(T, k, self.e_local)),
+                                      dtype=torch.uint8, device=device)
             if self.shared_I:
                 b.shared_offsets = torch.tensor([0, T], **i32)
                 b.shared_h = torch.empty((T, self.shared_I), **act)
-                b.shared_o = torch.empty((T, self.H), **act)
+                b.shared_o = torch.empty((T, self.H), dtype=self.o_dtype, device=device)
             self._buf[T] = b
         return b
 
@@ -120,7 +128,7 @@ class MoELayer:
         ops.route(logits, self.k, b.ids, b.w, stream=stream)
         ops.pack_routing(b.ids, b.w, b.blob, stream=stream)
         ops.permute(b.blob, self.e_first, self.e_local, b.sorted_pairs, b.group_offsets, b.pair_pos,
-                    stream=stream)
+                    workspace=b.workspace, stream=stream)
 
     def step_gate_up(self, x, b, stream=None):
         W = self.weights

@@ -56,18 +56,26 @@ def pack_routing(ids: torch.Tensor, w: torch.Tensor, blob: torch.Tensor | None =
     return blob
 
 
+def permute_workspace_bytes(T: int, k: int, e_local: int) -> int:
+    return int(load().moe_permute_workspace_bytes(T, k, e_local))
+
+
 def permute(blob: torch.Tensor, e_first: int, e_local: int, sorted_pairs=None, group_offsets=None,
-            pair_pos=None, stream=None):
+            pair_pos=None, workspace=None, stream=None):
     """blob [2][T][k] -> (sorted_pairs [T*k], group_offsets [e_local+1], pair_pos [T*k])."""
     _, T, k = blob.shape
     assert blob.dtype == torch.int32
     dev = blob.device
+    ws_bytes = permute_workspace_bytes(T, k, e_local)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     sp = sorted_pairs if sorted_pairs is not None else torch.empty(T * k, dtype=torch.int32, device=dev)
     off = group_offsets if group_offsets is not None else torch.empty(e_local + 1, dtype=torch.int32, device=dev)
     pp = pair_pos if pair_pos is not None else torch.empty(T * k, dtype=torch.int32, device=dev)
-    _dev(blob, sp, off, pp)
+    _dev(blob, sp, off, pp, workspace)
     check("moe_permute", load().moe_permute(_ptr(blob), T, k, e_first, e_local, _ptr(sp), _ptr(off),
-                                            _ptr(pp), _stream(stream)))
+                                            _ptr(pp), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
     return sp, off, pp
 
 
@@ -89,8 +97,8 @@ def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torc
     args.a_rows = a.shape[0]
     args.row_div = row_div
     args.m_hint = m_hint
-    args.reserved = 0
-    assert out.dtype == a.dtype and a.shape[1] == K and out.shape[1] == N
+    args.out_dtype = _DT[out.dtype]
+    assert a.shape[1] == K and out.shape[1] == N
     args.a, args.row_index, args.group_offsets = _ptr(a), _ptr(row_index), _ptr(group_offsets)
     args.w0, args.w1, args.s0, args.s1, args.out = _ptr(w0), _ptr(w1), _ptr(s0), _ptr(s1), _ptr(out)
     check("moe_grouped_gemm", load().moe_grouped_gemm(ctypes.byref(args), _stream(stream)))

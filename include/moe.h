@@ -107,12 +107,17 @@ moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T,
  *   group_offsets int32 [e_local+1]  out: group e owns rows [off[e], off[e+1]); off[0] = 0,
  *                                    off[e_local] = n_loc.
  *   pair_pos      int32 [T*k]        out: row of pair p in sorted_pairs, or -1 if p is not local.
+ *   workspace     device scratch of at least moe_permute_workspace_bytes(T, k, e_local) bytes
+ *                 (per-chunk expert counts); its contents on entry do not matter.  Calls that
+ *                 may run concurrently need separate workspaces.
  *   Limits: 1 <= T, 1 <= k <= 64, 1 <= e_local <= 1024, e_first >= 0, T * k < 2^31.
  *   Deterministic: the output does not depend on scheduling.
  */
+size_t moe_permute_workspace_bytes(int T, int k, int e_local);
+
 moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
                        int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_grouped_gemm -- one grouped GEMM over the experts of this device ("Systems engineering
@@ -123,8 +128,9 @@ moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_loc
  * A row a[row_index[r] / row_div] (or a[r] when row_index is NULL) and expert e's weights.
  * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg[e][k][n]) * (sum_k A[k] Wu[e][k][n]).
  * DOWN:           out[r][n] = sum_k A[k] Wd[e][k][n].
- * bf16 path: bf16 operands, fp32 accumulation, bf16 output (int4 weights are dequantised to bf16
- * in LDS).  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are not written.
+ * bf16 path: bf16 operands, fp32 accumulation, bf16 or (DOWN) fp32 output; int4 weights are
+ * dequantised to bf16 in LDS.  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are
+ * not written.
  */
 typedef struct moe_gemm_args {
   int32_t op;          /* moe_gemm_op */
@@ -139,7 +145,8 @@ typedef struct moe_gemm_args {
   int32_t a_rows;      /* rows of a (tokens for GATE_UP, rows_cap for DOWN) */
   int32_t row_div;     /* >= 1; divisor applied to row_index (k for GATE_UP after moe_permute) */
   int32_t m_hint;      /* expected rows per group, a launch-shape hint only (0: unknown) */
-  int32_t reserved;    /* must be 0 */
+  int32_t out_dtype;   /* moe_dtype of out: act_dtype, or MOE_DT_F32 for DOWN (fp32 partial
+                          outputs avoid a bf16 rounding of every expert output row) */
   const void* a;                 /* [a_rows][K] act dtype */
   const int32_t* row_index;      /* [rows_cap] (e.g. sorted_pairs) or NULL for identity rows */
   const int32_t* group_offsets;  /* [n_groups+1] non-decreasing, [0] = 0 (e.g. from moe_permute) */
@@ -147,7 +154,7 @@ typedef struct moe_gemm_args {
   const void* w1;      /* GATE_UP: Wu (same layout as w0); DOWN: NULL */
   const void* s0;      /* int4: bf16 scales of w0 [n_groups][K/group_size][N]; dense: NULL */
   const void* s1;      /* int4: bf16 scales of w1; otherwise NULL */
-  void* out;           /* [rows_cap][N] act dtype */
+  void* out;           /* [rows_cap][N] out_dtype */
 } moe_gemm_args;
 
 moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
@@ -160,7 +167,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
  *   blob        int32 [2][T][k]              weights are read from plane 1.
  *   pair_pos    int32 [T*k]                  from moe_permute; -1 (or any value outside
  *                                            [0, expert_rows)) marks a pair without a row.
- *   shared_out  [T][H] act dtype or NULL.
+ *   shared_out  [T][H] act dtype or NULL (same dtype as expert_out).
  *   y           [T][H] y_dtype               out: y[t] = sum_{j ascending, valid pair_pos}
  *                                            w[t][j] * expert_out[pair_pos[t*k+j]]
  *                                            (+ shared_out[t]), accumulated in fp32 in that

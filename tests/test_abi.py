@@ -67,18 +67,24 @@ def test_pack_and_permute_validation(L):
     assert L.moe_pack_routing(FAKE, FAKE, 4, 65, FAKE, None) == INV
     assert L.moe_pack_routing(FAKE, FAKE, 0, 2, FAKE, None) == INV
     assert L.moe_pack_routing(FAKE, FAKE, 1 << 26, 64, FAKE, None) == INV
-    assert L.moe_permute(None, 4, 2, 0, 8, FAKE, FAKE, FAKE, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, None, FAKE, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 0, FAKE, FAKE, FAKE, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 1025, FAKE, FAKE, FAKE, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, -1, 8, FAKE, FAKE, FAKE, None) == INV
-    assert L.moe_permute(FAKE, 4, 0, 0, 8, FAKE, FAKE, FAKE, None) == INV
+    ws = L.moe_permute_workspace_bytes(4, 2, 8)
+    assert ws == 8 * 4                                    # one chunk of per-expert counts
+    assert L.moe_permute_workspace_bytes(8192, 10, 64) == 40 * 64 * 4
+    assert L.moe_permute_workspace_bytes(0, 2, 8) == 0
+    assert L.moe_permute(None, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, None, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 1025, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, -1, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 0, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, None, ws, None) == INV
+    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == INV
 
 
 def _gemm(**kw):
     a = MoeGemmArgs()
     base = dict(op=0, act_dtype=1, wfmt=0, group_size=0, K=256, N=128, n_groups=8, rows_cap=64,
-                a_rows=32, row_div=2, m_hint=0, reserved=0, a=FAKE, row_index=FAKE, group_offsets=FAKE,
+                a_rows=32, row_div=2, m_hint=0, out_dtype=1, a=FAKE, row_index=FAKE, group_offsets=FAKE,
                 w0=FAKE, w1=FAKE, s0=None, s1=None, out=FAKE)
     base.update(kw)
     for k, v in base.items():
@@ -87,13 +93,14 @@ def _gemm(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(op=2), INV), (dict(act_dtype=7), UNS), (dict(wfmt=5), UNS), (dict(reserved=1), INV),
+    (dict(op=2), INV), (dict(act_dtype=7), UNS), (dict(wfmt=5), UNS), (dict(out_dtype=0), INV),
+    (dict(out_dtype=4), UNS), (dict(act_dtype=0, out_dtype=1), INV),
     (dict(a=None), INV), (dict(group_offsets=None), INV), (dict(w0=None), INV), (dict(out=None), INV),
     (dict(w1=None), INV), (dict(op=1, K=128, N=256, w1=FAKE), INV), (dict(K=32), INV), (dict(K=96), INV),
     (dict(N=32), INV), (dict(N=96), INV), (dict(op=1, K=128, N=192, w1=None), INV),
     (dict(n_groups=0), INV), (dict(n_groups=1025), INV), (dict(rows_cap=0), INV), (dict(a_rows=0), INV),
     (dict(row_div=0), INV), (dict(m_hint=-1), INV), (dict(row_index=None, a_rows=10), INV),
-    (dict(wfmt=1, act_dtype=0, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, act_dtype=0, out_dtype=0, group_size=128, s0=FAKE, s1=FAKE), UNS),
     (dict(wfmt=1, group_size=32, s0=FAKE, s1=FAKE), UNS),
     (dict(wfmt=1, group_size=96, s0=FAKE, s1=FAKE), UNS),
     (dict(wfmt=1, K=192, group_size=128, s0=FAKE, s1=FAKE), UNS),

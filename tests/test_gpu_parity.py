@@ -50,7 +50,7 @@ def _check_close(got, ref, what=""):
     assert mx <= MAX_ABS_RMS * rms, mx / rms
 
 
-def _run(cfg, inp, y_dtype=None, m_hint=None):
+def _run(cfg, inp, y_dtype=torch.float32, m_hint=None):
     x, logits, wts = upload(inp, cfg, _dev())
     layer = MoELayer.from_config(cfg, wts, y_dtype=y_dtype)
     if m_hint is not None:
@@ -142,7 +142,7 @@ MID = {
                                shared_I=320),
     "int4_g128": W.MoEConfig("mid", T=280, H=512, E=32, k=4, I=256, e_first=0, e_local=16,
                              wfmt="int4", group_size=128),
-    "int4_g64_channel": W.MoEConfig("mid", T=150, H=256, E=16, k=3, I=256, e_first=2, e_local=8,
+    "int4_channel": W.MoEConfig("mid", T=150, H=256, E=16, k=3, I=256, e_first=2, e_local=8,
                                     wfmt="int4", group_size=256),
     "f32": W.MoEConfig("mid", T=130, H=256, E=12, k=3, I=192, e_first=1, e_local=9, act="f32"),
     "f32_shared": W.MoEConfig("mid", T=70, H=128, E=8, k=2, I=64, e_first=0, e_local=8, act="f32",
@@ -170,7 +170,7 @@ def test_layer_bf16_output_and_determinism():
     cfg = MID["bf16_ragged"]
     inp = W.make_inputs(cfg)
     x, logits, wts = upload(inp, cfg, _dev())
-    layer = MoELayer.from_config(cfg, wts)
+    layer = MoELayer.from_config(cfg, wts, y_dtype=torch.bfloat16)
     y1 = layer.forward(x, logits).clone()
     y2 = layer.forward(x, logits).clone()
     torch.cuda.synchronize()
@@ -208,8 +208,7 @@ def _sample_tokens(cfg, ids, n=40):
 def test_layer_full_workload_sampled(name):
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg)
-    y_dtype = torch.float32 if cfg.act == "f32" else torch.bfloat16
-    layer, b, y = _run(cfg, inp, y_dtype=y_dtype)
+    layer, b, y = _run(cfg, inp)
     ids, w, off = _check_routing(b, inp, cfg)
     toks, loc = _sample_tokens(cfg, ids)
     ref = oracle.layer(inp, cfg, ids, w, tokens=toks, threads=8)
