@@ -176,14 +176,15 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     const int mt_live = min(MT, max(0, (rows - wrow0 + 15) / 16));
 
     // ---- per-thread global sources -----------------------------------------------------------
+    // Every load is unconditional (padding rows repeat the last valid row; the prefetch past the
+    // last chunk re-reads it): a branch around a load would make the compiler wait for all
+    // outstanding loads, including the chunks prefetched ahead.
     const u16* a_src[C::A_LOADS];
     int a_lds[C::A_LOADS];
-    bool a_ok[C::A_LOADS];
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int c = tid + 256 * i;
       const int r = c / (KC / 8), kc8 = c % (KC / 8);
-      a_ok[i] = r < rows;                                   // padding rows are never loaded
       const int rr = row0 + min(r, rows - 1);
       int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
@@ -217,9 +218,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     }
 
     auto load_chunk = [&](int kc, Chunk<C>& ch) {
+      kc = min(kc, nK - 1);
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
-        if (a_ok[i]) ch.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kc * KC);
+        ch.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kc * KC);
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
         if constexpr (!C::Q4) {
@@ -240,8 +242,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
       u16* sA = buf;
       u16* sB = buf + C::A_ELEMS;
 #pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i)
-        if (a_ok[i]) *reinterpret_cast<u32x4*>(sA + a_lds[i]) = ch.a[i];
+      for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + a_lds[i]) = ch.a[i];
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
         if constexpr (!C::Q4) {
@@ -314,43 +315,43 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     // buffer is refilled between two barriers.
     Chunk<C> c0, c1;
     load_chunk(0, c0);
-    if (nK > 1) load_chunk(1, c1);
+    load_chunk(1, c1);
+    int kc = 0;
     if constexpr (C::STAGES == 2) {
       store_chunk(c0, buf0);
-      if (nK > 2) load_chunk(2, c0);
+      load_chunk(2, c0);
       __syncthreads();
-      for (int kc = 0; kc < nK; kc += 2) {
+      for (; kc + 1 < nK; kc += 2) {               // straight-line body: chunks kc and kc + 1
         compute(buf0);
-        if (kc + 1 < nK) {
-          store_chunk(c1, buf1);
-          if (kc + 3 < nK) load_chunk(kc + 3, c1);
-        }
+        store_chunk(c1, buf1);
+        load_chunk(kc + 3, c1);
         __syncthreads();
-        if (kc + 1 < nK) {
-          compute(buf1);
-          if (kc + 2 < nK) {
-            store_chunk(c0, buf0);
-            if (kc + 4 < nK) load_chunk(kc + 4, c0);
-          }
-          __syncthreads();
-        }
+        compute(buf1);
+        store_chunk(c0, buf0);
+        load_chunk(kc + 4, c0);
+        __syncthreads();
       }
+      if (kc < nK) compute(buf0);                  // odd chunk count: the last chunk
     } else {
-      for (int kc = 0; kc < nK; kc += 2) {
+      for (; kc + 1 < nK; kc += 2) {
         store_chunk(c0, buf0);
         __syncthreads();
-        if (kc + 2 < nK) load_chunk(kc + 2, c0);
+        load_chunk(kc + 2, c0);
         compute(buf0);
         __syncthreads();
-        if (kc + 1 < nK) {
-          store_chunk(c1, buf0);
-          __syncthreads();
-          if (kc + 3 < nK) load_chunk(kc + 3, c1);
-          compute(buf0);
-          __syncthreads();
-        }
+        store_chunk(c1, buf0);
+        __syncthreads();
+        load_chunk(kc + 3, c1);
+        compute(buf0);
+        __syncthreads();
+      }
+      if (kc < nK) {
+        store_chunk(c0, buf0);
+        __syncthreads();
+        compute(buf0);
       }
     }
+    __syncthreads();                               // LDS is refilled by the next tile
 
     // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile ----------
 #pragma unroll

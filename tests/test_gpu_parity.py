@@ -166,19 +166,25 @@ def test_layer_mid_size_every_token(name, variant):
         assert np.all(_np(y)[counts == 0] == 0.0)
 
 
-def test_layer_bf16_output_and_determinism():
+def test_layer_bf16_output_is_rounded_fp32_output_and_deterministic():
+    """The bf16 layer output is the round-to-nearest-even of the fp32 output (the combine
+    accumulates in fp32 either way), and repeated calls are bitwise identical."""
     cfg = MID["bf16_ragged"]
     inp = W.make_inputs(cfg)
     x, logits, wts = upload(inp, cfg, _dev())
-    layer = MoELayer.from_config(cfg, wts, y_dtype=torch.bfloat16)
-    y1 = layer.forward(x, logits).clone()
-    y2 = layer.forward(x, logits).clone()
+    l32 = MoELayer.from_config(cfg, wts, y_dtype=torch.float32)
+    l16 = MoELayer.from_config(cfg, wts, y_dtype=torch.bfloat16)
+    y32a = l32.forward(x, logits).clone()
+    y16a = l16.forward(x, logits).clone()
+    y32b = l32.forward(x, logits).clone()
+    y16b = l16.forward(x, logits).clone()
     torch.cuda.synchronize()
-    assert y1.dtype == torch.bfloat16
-    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y32a.view(torch.int32), y32b.view(torch.int32))
+    assert torch.equal(y16a.view(torch.int16), y16b.view(torch.int16))
+    assert torch.equal(y16a.view(torch.int16), y32a.to(torch.bfloat16).view(torch.int16))
     ids, w = oracle.route(inp["logits"], cfg.k)
     ref = oracle.layer(inp, cfg, ids, w, threads=8)
-    _check_close(y1.float().cpu().numpy().astype(np.float64), ref, "bf16 out")
+    _check_close(y32a.cpu().numpy().astype(np.float64), ref, "fp32 out")
 
 
 def test_layer_single_token_and_single_expert():
