@@ -104,26 +104,38 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // ---------------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_>
+// Raw buffer resource (gfx9 family dword 3): weight loads use one scalar descriptor per tile
+// plus 32-bit per-lane byte offsets.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int WGS = WGS_;                  // intended workgroups per CU
+  static constexpr int WAVES_PER_SIMD = (WM_ * WN_ * WGS_ + 3) / 4;   // register budget target
   static constexpr bool GU = GU_, Q4 = Q4_;
-  static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
+  static constexpr int NWAVES = WM * WN, NT = 64 * NWAVES;    // threads per workgroup
   static constexpr int KC = 64;                     // K chunk per LDS stage
   static constexpr int NW = GU ? 2 : 1;             // weight matrices
   static constexpr int LDK = KC + 8;                // padded LDS row (bf16 elements): 144 bytes
   static constexpr int A_ELEMS = BM * LDK;
   static constexpr int B_ELEMS = NW * BN * LDK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;   // u16 elements per LDS buffer
-  static constexpr int A_LOADS = BM * (KC / 8) / 256;          // 16-byte A chunks per thread
+  static constexpr int A_CHUNKS = BM * (KC / 8);    // 16-byte pieces of the A tile
+  static constexpr int A_LOADS = A_CHUNKS >= NT ? A_CHUNKS / NT : 1;   // per thread (small tiles: duplicated)
   // B units per thread: a dense R x 8 block or one 16-byte row of 4 int4 words, 32 weights each
-  static constexpr int B_UNITS = NW * KC * BN / 32 / 256;
+  static constexpr int B_UNITS = NW * KC * BN / 32 / NT;
   static constexpr int R = 4;                       // dense: k-rows per transposed block
   static constexpr int MT = BM / WM / 16;           // 16-row MFMA tiles per wave
   static constexpr int NTL = BN / WN / 16;          // 16-column MFMA tiles per wave and matrix
-  static_assert(WM * WN == 4, "four waves");
-  static_assert(A_LOADS >= 1 && BM * (KC / 8) % 256 == 0, "A tile split");
-  static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * 256) == 0, "B tile split");
+  static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves");
+  static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
+  static_assert(A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0, "A tile split");
+  static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * NT) == 0, "B tile split");
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
@@ -136,20 +148,214 @@ struct Chunk {
   u32x2 s[C::B_UNITS];
 };
 
+// Everything a thread needs to move one tile's chunks: gathered A row pointers, the weight and
+// scale descriptors of the tile's expert and its own byte offsets, and LDS destinations.
+template <class C>
+struct TileCtx {
+  const u16* a_src[C::A_LOADS];
+  int a_lds[C::A_LOADS];
+  __amdgpu_buffer_rsrc_t wr[C::B_UNITS];          // descriptor of the matrix each unit reads
+  __amdgpu_buffer_rsrc_t sr[C::B_UNITS];
+  uint32_t b_off[C::B_UNITS];
+  uint32_t s_off[C::B_UNITS];
+  int b_lds[C::B_UNITS];
+  int nK, row_bytes, s_row_bytes, group_size;
+};
+
+template <class C>
+__device__ __forceinline__ void load_chunk(const TileCtx<C>& t, int kc, Chunk<C>& ch) {
+  kc = min(kc, t.nK - 1);                           // unconditional loads: a branch around a load
+                                                    // would make the compiler drain the prefetch
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i)
+    ch.a[i] = *reinterpret_cast<const u32x4*>(t.a_src[i] + (size_t)kc * C::KC);
+#pragma unroll
+  for (int i = 0; i < C::B_UNITS; ++i) {
+    if constexpr (!C::Q4) {
+#pragma unroll
+      for (int r = 0; r < C::R; ++r)
+        ch.b[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
+            t.wr[i], t.b_off[i] + (uint32_t)(kc * C::KC + r) * t.row_bytes, 0, 2 /* nontemporal */);
+    } else {
+      ch.b[i][0] = __builtin_amdgcn_raw_buffer_load_b128(
+          t.wr[i], t.b_off[i] + (uint32_t)(kc * (C::KC / 8)) * t.row_bytes, 0, 2);
+      const int grp = (kc * C::KC) / t.group_size;
+      ch.s[i] = __builtin_amdgcn_raw_buffer_load_b64(t.sr[i], t.s_off[i] + (uint32_t)grp * t.s_row_bytes, 0, 0);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>& ch, u16* buf) {
+  u16* sA = buf;
+  u16* sB = buf + C::A_ELEMS;
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + t.a_lds[i]) = ch.a[i];
+#pragma unroll
+  for (int i = 0; i < C::B_UNITS; ++i) {
+    if constexpr (!C::Q4) {
+      // ch.b[i][r] = k-row r, dword d = columns (2d, 2d+1); column c gets k-rows 0..3.
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int d = c >> 1;
+        uint32_t lo, hi;
+        if (c & 1) {
+          lo = pack_hi16(ch.b[i][0][d], ch.b[i][1][d]);
+          hi = pack_hi16(ch.b[i][2][d], ch.b[i][3][d]);
+        } else {
+          lo = pack_lo16(ch.b[i][0][d], ch.b[i][1][d]);
+          hi = pack_lo16(ch.b[i][2][d], ch.b[i][3][d]);
+        }
+        *reinterpret_cast<u32x2*>(sB + t.b_lds[i] + c * C::LDK) = u32x2{lo, hi};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t word = ch.b[i][0][c];
+        const uint32_t sbits = (c & 1) ? (ch.s[i][c >> 1] >> 16) : (ch.s[i][c >> 1] & 0xffffu);
+        const float sc = __uint_as_float(sbits << 16);
+        uint32_t q[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int q0 = ((int)(word << (28 - 8 * h))) >> 28;        // nibble 2h
+          const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
+          q[h] = pack_bf16x2((float)q0 * sc, (float)q1 * sc);
+        }
+        *reinterpret_cast<u32x4*>(sB + t.b_lds[i] + c * C::LDK) = u32x4{q[0], q[1], q[2], q[3]};
+      }
+    }
+  }
+}
+
+// MFMAs of one LDS chunk for the NM live 16-row tiles of this wave.
+template <class C, int NM>
+__device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW][NM > 0 ? NM : 1][C::NTL],
+                                              int arow, int bcol, int kofs) {
+  if constexpr (NM > 0) {
+    const u16* sA = buf;
+    const u16* sB = buf + C::A_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < C::KC; ks += 32) {
+      bf16x8 av[NM];
+#pragma unroll
+      for (int i = 0; i < NM; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 16) * C::LDK + ks + kofs);
+#pragma unroll
+      for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+        for (int j = 0; j < C::NTL; ++j) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + (m * C::BN + bcol + j * 16) * C::LDK + ks + kofs);
+#pragma unroll
+          for (int i = 0; i < NM; ++i)
+            acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
+        }
+    }
+  }
+}
+
+// K loop and epilogue of one tile for a wave with NM live 16-row tiles.  Every wave runs the same
+// loads, LDS stores and barriers whatever its NM.
+template <class C, typename OutT, int NM>
+__device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* buf1, OutT* O, int N, int lane,
+                                          int wrow0, int wcol0, int row0, int rows, int n0) {
+  f32x4 acc[C::NW][NM > 0 ? NM : 1][C::NTL];
+#pragma unroll
+  for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+    for (int i = 0; i < (NM > 0 ? NM : 1); ++i)
+#pragma unroll
+      for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int arow = wrow0 + (lane & 15);
+  const int bcol = wcol0 + (lane & 15);
+  const int kofs = (lane >> 4) * 8;
+  const int nK = t.nK;
+
+  // Loads run two chunks ahead of the MFMAs (two register sets).  With two LDS buffers one
+  // barrier per chunk suffices; with one buffer it is refilled between two barriers.
+  Chunk<C> c0, c1;
+  load_chunk(t, 0, c0);
+  load_chunk(t, 1, c1);
+  int kc = 0;
+  if constexpr (C::STAGES == 2) {
+    store_chunk(t, c0, buf0);
+    load_chunk(t, 2, c0);
+    __syncthreads();
+    for (; kc + 1 < nK; kc += 2) {                 // straight-line body: chunks kc and kc + 1
+      compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+      store_chunk(t, c1, buf1);
+      load_chunk(t, kc + 3, c1);
+      __syncthreads();
+      compute_chunk<C, NM>(buf1, acc, arow, bcol, kofs);
+      store_chunk(t, c0, buf0);
+      load_chunk(t, kc + 4, c0);
+      __syncthreads();
+    }
+    if (kc < nK) compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+  } else {
+    for (; kc + 1 < nK; kc += 2) {
+      store_chunk(t, c0, buf0);
+      __syncthreads();
+      load_chunk(t, kc + 2, c0);
+      compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+      __syncthreads();
+      store_chunk(t, c1, buf0);
+      __syncthreads();
+      load_chunk(t, kc + 3, c1);
+      compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+      __syncthreads();
+    }
+    if (kc < nK) {
+      store_chunk(t, c0, buf0);
+      __syncthreads();
+      compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+    }
+  }
+  __syncthreads();                                 // LDS is refilled by the next tile
+
+  // epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
+#pragma unroll
+  for (int i = 0; i < NM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wrow0 + i * 16 + (lane >> 4) * 4 + r;
+        const int col = wcol0 + j * 16 + (lane & 15);
+        if (row < rows) {
+          float v;
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
+          else v = acc[0][i][j][r];
+          OutT* dst = O + (size_t)(row0 + row) * N + n0 + col;
+          if constexpr (sizeof(OutT) == 4) *dst = v;
+          else *dst = f32_to_bf16(v);
+        }
+      }
+}
+
+template <class C, typename OutT, int NM>
+__device__ __forceinline__ void tile_dispatch(int nm, const TileCtx<C>& t, u16* buf0, u16* buf1, OutT* O, int N,
+                                              int lane, int wrow0, int wcol0, int row0, int rows, int n0) {
+  if constexpr (NM <= C::MT) {
+    if (nm == NM) tile_body<C, OutT, NM>(t, buf0, buf1, O, N, lane, wrow0, wcol0, row0, rows, n0);
+    else tile_dispatch<C, OutT, NM + 1>(nm, t, buf0, buf1, O, N, lane, wrow0, wcol0, row0, rows, n0);
+  }
+}
+
 template <class C, typename OutT>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
-  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, KC = C::KC, NW = C::NW, LDK = C::LDK;
-  constexpr int MT = C::MT, NTL = C::NTL;
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD)))
+void k_gemm_bf16(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, KC = C::KC, LDK = C::LDK, NT = C::NT;
   extern __shared__ __attribute__((aligned(16))) u16 smem[];
   u16* buf0 = smem;
   u16* buf1 = smem + (C::STAGES - 1) * C::STAGE;
   int* s_tstart = reinterpret_cast<int*>(smem + C::STAGES * C::STAGE);
   int* s_goff = s_tstart + (p.n_groups + 1);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = p.N / BN;
-  const int nK = p.K / KC;
+  const int wrow0 = wm * (BM / WM), wcol0 = wn * (BN / WN);
 
   build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
   __syncthreads();
@@ -158,9 +364,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
 
   const u16* A = static_cast<const u16*>(p.a);
   OutT* O = static_cast<OutT*>(p.out);
-  const int arow = wm * (BM / WM) + (lane & 15);
-  const int bcol = wn * (BN / WN) + (lane & 15);
-  const int kofs = (lane >> 4) * 8;
+  const uint32_t w_bytes = C::Q4 ? (uint32_t)((size_t)p.K / 8 * p.N * 4) : (uint32_t)((size_t)p.K * p.N * 2);
+  const uint32_t s_bytes = C::Q4 ? (uint32_t)((size_t)(p.K / p.group_size) * p.N * 2) : 0u;
 
   for (int tile = it.next; tile < it.end; tile += it.step) {
     const int e = find_group(s_tstart, p.n_groups, tile);
@@ -171,208 +376,59 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     const int row0 = g0 + mt * BM;
     const int rows = min(BM, g1 - row0);
     const int n0 = nt * BN;
-    // 16-row MFMA tiles of this wave that hold at least one valid row
-    const int wrow0 = wm * (BM / WM);
-    const int mt_live = min(MT, max(0, (rows - wrow0 + 15) / 16));
+    const int nm = min(C::MT, max(0, (rows - wrow0 + 15) / 16));   // live 16-row tiles of this wave
 
-    // ---- per-thread global sources -----------------------------------------------------------
-    // Every load is unconditional (padding rows repeat the last valid row; the prefetch past the
-    // last chunk re-reads it): a branch around a load would make the compiler wait for all
-    // outstanding loads, including the chunks prefetched ahead.
-    const u16* a_src[C::A_LOADS];
-    int a_lds[C::A_LOADS];
+    TileCtx<C> t;
+    t.nK = p.K / KC;
+    t.group_size = p.group_size;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
-      const int c = tid + 256 * i;
+      const int c = (tid + NT * i) % C::A_CHUNKS;
       const int r = c / (KC / 8), kc8 = c % (KC / 8);
-      const int rr = row0 + min(r, rows - 1);
+      const int rr = row0 + min(r, rows - 1);          // padding rows repeat the last valid row
       int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
-      a_src[i] = A + (size_t)src * p.K + kc8 * 8;
-      a_lds[i] = r * LDK + kc8 * 8;
+      t.a_src[i] = A + (size_t)src * p.K + kc8 * 8;
+      t.a_lds[i] = r * LDK + kc8 * 8;
     }
-    const char* b_src[C::B_UNITS];
-    const u16* s_src[C::B_UNITS];
-    int b_lds[C::B_UNITS];
+    // Unit i of a thread reads matrix (tid + NT*i) / per_m, the same for the whole wave.
+    constexpr int per_m = KC * BN / 32;
+    static_assert(per_m % 64 == 0, "a wave's units read one matrix");
 #pragma unroll
     for (int i = 0; i < C::B_UNITS; ++i) {
-      const int u = tid + 256 * i;
-      if constexpr (!C::Q4) {
-        constexpr int per_m = (KC / C::R) * (BN / 8);
-        const int m = u / per_m, v = u % per_m;
-        const int nb = v % (BN / 8), kb = v / (BN / 8);
-        const u16* W = static_cast<const u16*>(m == 0 ? p.w0 : p.w1);
-        b_src[i] = reinterpret_cast<const char*>(W + ((size_t)e * p.K + kb * C::R) * p.N + n0 + nb * 8);
-        b_lds[i] = (m * BN + nb * 8) * LDK + kb * C::R;
-        s_src[i] = nullptr;
-      } else {
-        constexpr int per_m = (KC / 8) * (BN / 4);
-        const int m = u / per_m, v = u % per_m;
-        const int nq = v % (BN / 4), kw = v / (BN / 4);
-        const int32_t* Wq = static_cast<const int32_t*>(m == 0 ? p.w0 : p.w1);
-        const u16* S = static_cast<const u16*>(m == 0 ? p.s0 : p.s1);
-        b_src[i] = reinterpret_cast<const char*>(Wq + ((size_t)e * (p.K / 8) + kw) * p.N + n0 + nq * 4);
-        s_src[i] = S + (size_t)e * (p.K / p.group_size) * p.N + n0 + nq * 4;
-        b_lds[i] = (m * BN + nq * 4) * LDK + kw * 8;
+      const int m = __builtin_amdgcn_readfirstlane((tid + NT * i) / per_m);
+      const char* W = static_cast<const char*>(m == 0 ? p.w0 : p.w1);
+      t.wr[i] = make_rsrc(W + (size_t)e * w_bytes, w_bytes);
+      if constexpr (C::Q4) {
+        const char* S = static_cast<const char*>(m == 0 ? p.s0 : p.s1);
+        t.sr[i] = make_rsrc(S + (size_t)e * s_bytes, s_bytes);
       }
     }
-
-    auto load_chunk = [&](int kc, Chunk<C>& ch) {
-      kc = min(kc, nK - 1);
-#pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i)
-        ch.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kc * KC);
+    if constexpr (!C::Q4) {
+      t.row_bytes = p.N * 2;
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
-        if constexpr (!C::Q4) {
-#pragma unroll
-          for (int r = 0; r < C::R; ++r)
-            ch.b[i][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                b_src[i] + ((size_t)kc * KC + r) * p.N * sizeof(u16)));
-        } else {
-          ch.b[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              b_src[i] + (size_t)kc * (KC / 8) * p.N * sizeof(int32_t)));
-          const int grp = (kc * KC) / p.group_size;
-          ch.s[i] = *reinterpret_cast<const u32x2*>(s_src[i] + (size_t)grp * p.N);
-        }
+        const int u = (tid + NT * i) % per_m;
+        const int nb = u % (BN / 8), kb = u / (BN / 8);
+        const int m = (tid + NT * i) / per_m;
+        t.b_off[i] = (uint32_t)((kb * C::R) * p.N + n0 + nb * 8) * 2u;
+        t.b_lds[i] = (m * BN + nb * 8) * LDK + kb * C::R;
+        t.s_off[i] = 0;
       }
-    };
-
-    auto store_chunk = [&](const Chunk<C>& ch, u16* buf) {
-      u16* sA = buf;
-      u16* sB = buf + C::A_ELEMS;
-#pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + a_lds[i]) = ch.a[i];
-#pragma unroll
-      for (int i = 0; i < C::B_UNITS; ++i) {
-        if constexpr (!C::Q4) {
-          // ch.b[i][r] = k-row r, dword d = columns (2d, 2d+1); column c gets k-rows 0..3.
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int d = c >> 1;
-            uint32_t lo, hi;
-            if (c & 1) {
-              lo = pack_hi16(ch.b[i][0][d], ch.b[i][1][d]);
-              hi = pack_hi16(ch.b[i][2][d], ch.b[i][3][d]);
-            } else {
-              lo = pack_lo16(ch.b[i][0][d], ch.b[i][1][d]);
-              hi = pack_lo16(ch.b[i][2][d], ch.b[i][3][d]);
-            }
-            *reinterpret_cast<u32x2*>(sB + b_lds[i] + c * LDK) = u32x2{lo, hi};
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t word = ch.b[i][0][c];
-            const uint32_t sbits = (c & 1) ? (ch.s[i][c >> 1] >> 16) : (ch.s[i][c >> 1] & 0xffffu);
-            const float sc = __uint_as_float(sbits << 16);
-            uint32_t q[4];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const int q0 = ((int)(word << (28 - 8 * h))) >> 28;        // nibble 2h
-              const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
-              q[h] = pack_bf16x2((float)q0 * sc, (float)q1 * sc);
-            }
-            *reinterpret_cast<u32x4*>(sB + b_lds[i] + c * LDK) = u32x4{q[0], q[1], q[2], q[3]};
-          }
-        }
-      }
-    };
-
-    f32x4 acc[NW][MT][NTL];
-#pragma unroll
-    for (int m = 0; m < NW; ++m)
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](const u16* buf) {
-      const u16* sA = buf;
-      const u16* sB = buf + C::A_ELEMS;
-#pragma unroll
-      for (int ks = 0; ks < KC; ks += 32) {
-        bf16x8 av[MT];
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-          if (i < mt_live) av[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 16) * LDK + ks + kofs);
-#pragma unroll
-        for (int m = 0; m < NW; ++m)
-#pragma unroll
-          for (int j = 0; j < NTL; ++j) {
-            const bf16x8 bv =
-                *reinterpret_cast<const bf16x8*>(sB + (m * BN + bcol + j * 16) * LDK + ks + kofs);
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-              if (i < mt_live)
-                acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
-          }
-      }
-    };
-
-    // ---- K loop: loads run two chunks ahead of the MFMAs (two register sets).  With two LDS
-    // buffers one barrier per chunk suffices; with one buffer (more workgroups per CU) the
-    // buffer is refilled between two barriers.
-    Chunk<C> c0, c1;
-    load_chunk(0, c0);
-    load_chunk(1, c1);
-    int kc = 0;
-    if constexpr (C::STAGES == 2) {
-      store_chunk(c0, buf0);
-      load_chunk(2, c0);
-      __syncthreads();
-      for (; kc + 1 < nK; kc += 2) {               // straight-line body: chunks kc and kc + 1
-        compute(buf0);
-        store_chunk(c1, buf1);
-        load_chunk(kc + 3, c1);
-        __syncthreads();
-        compute(buf1);
-        store_chunk(c0, buf0);
-        load_chunk(kc + 4, c0);
-        __syncthreads();
-      }
-      if (kc < nK) compute(buf0);                  // odd chunk count: the last chunk
     } else {
-      for (; kc + 1 < nK; kc += 2) {
-        store_chunk(c0, buf0);
-        __syncthreads();
-        load_chunk(kc + 2, c0);
-        compute(buf0);
-        __syncthreads();
-        store_chunk(c1, buf0);
-        __syncthreads();
-        load_chunk(kc + 3, c1);
-        compute(buf0);
-        __syncthreads();
-      }
-      if (kc < nK) {
-        store_chunk(c0, buf0);
-        __syncthreads();
-        compute(buf0);
+      t.row_bytes = p.N * 4;
+      t.s_row_bytes = p.N * 2;
+#pragma unroll
+      for (int i = 0; i < C::B_UNITS; ++i) {
+        const int u = (tid + NT * i) % per_m;
+        const int nq = u % (BN / 4), kw = u / (BN / 4);
+        const int m = (tid + NT * i) / per_m;
+        t.b_off[i] = (uint32_t)(kw * p.N + n0 + nq * 4) * 4u;
+        t.s_off[i] = (uint32_t)(n0 + nq * 4) * 2u;
+        t.b_lds[i] = (m * BN + nq * 4) * LDK + kw * 8;
       }
     }
-    __syncthreads();                               // LDS is refilled by the next tile
-
-    // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile ----------
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if (i >= mt_live) break;
-#pragma unroll
-      for (int j = 0; j < NTL; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wrow0 + i * 16 + (lane >> 4) * 4 + r;
-          const int col = wn * (BN / WN) + j * 16 + (lane & 15);
-          if (row < rows) {
-            float v;
-            if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
-            else v = acc[0][i][j][r];
-            OutT* dst = O + (size_t)(row0 + row) * p.N + n0 + col;
-            if constexpr (sizeof(OutT) == 4) *dst = v;
-            else *dst = f32_to_bf16(v);
-          }
-        }
-    }
+    tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0);
   }
 }
 
@@ -460,7 +516,7 @@ hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  k_gemm_bf16<C, OutT><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
+  k_gemm_bf16<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
   return hipGetLastError();
 }
 
@@ -487,18 +543,28 @@ struct Variant {
   int bm, bn, wgs_per_cu;
 };
 
-template <int BM, int BN, int WM, int WN, int ST>
+// Whether a tile shape splits evenly over its workgroup (mirrors the static checks of Cfg).
+template <int BM, int BN, int WM, int WN, bool GU>
+constexpr bool cfg_ok() {
+  constexpr int NT = 64 * WM * WN, NW = GU ? 2 : 1, A_CHUNKS = BM * 8;
+  return (WM * WN == 4 || WM * WN == 8) && (NW * 64 * BN) % (32 * NT) == 0 && NW * 64 * BN >= 32 * NT &&
+         (A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0) && BM / WM >= 16 && BN / WN >= 16;
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int WGS>
 hipError_t run_variant(const GemmParams& p, bool gu, bool q4, bool f32out, int wgs, hipStream_t s) {
   if (gu) {
-    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true>, u16>(p, wgs, s)
-              : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false>, u16>(p, wgs, s);
+    if constexpr (cfg_ok<BM, BN, WM, WN, true>())
+      return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS>, u16>(p, wgs, s)
+                : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS>, u16>(p, wgs, s);
+    return hipErrorInvalidValue;
   }
-  if constexpr (BN >= 128) {
+  if constexpr (cfg_ok<BM, BN, WM, WN, false>()) {
     if (f32out)
-      return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true>, float>(p, wgs, s)
-                : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false>, float>(p, wgs, s);
-    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true>, u16>(p, wgs, s)
-              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false>, u16>(p, wgs, s);
+      return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, float>(p, wgs, s)
+                : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, float>(p, wgs, s);
+    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, u16>(p, wgs, s)
+              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, u16>(p, wgs, s);
   }
   return hipErrorInvalidValue;
 }
@@ -521,34 +587,42 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  // variant ids (rows x columns per tile for gate/up | down, LDS buffers, workgroups per CU):
-  //   0: 32x64|32x128, 1 buffer, 4     1: 32x128|32x256, 1 buffer, 4    2: 128x64|128x128, 2, 2
-  //   3: 128x128|128x256, 2, 1         4: 64x64|64x128, 2, 3            5: 32x64|32x128, 2, 3
-  int v = small_m ? 0 : 2;
+  // Variant ids: rows x columns per tile for gate/up | down, waves per workgroup, LDS buffers,
+  // workgroups per CU.
+  //   0: 32x64 | 32x128,   4 waves, 1 buffer, 4/CU     1: 32x128 | 32x256, 8 waves, 1 buffer, 2/CU
+  //   2: 128x64 | 128x128, 4 waves, 2 buffers, 2/CU    3: 128x128 | 128x256, 8 waves, 2 buffers, 1/CU
+  //   4: 64x64 | 64x128,   4 waves, 2 buffers, 3/CU    5: 32x128 | 32x256, 4 waves, 1 buffer, 2/CU
+  //   6: 128x128 | 128x256, 8 waves (4x2), 2 buffers, 1/CU
+  int v = small_m ? 1 : 2;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
   const int wgs = env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0);
   const bool n256 = p.N % 256 == 0;
   switch (v) {
+    case 0:
+      return gu ? run_variant<32, 64, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s)
+                : run_variant<32, 128, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s);
     case 1:
-      return gu ? run_variant<32, 128, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s)
-                : (n256 ? run_variant<32, 256, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s)
-                        : run_variant<32, 128, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s));
-    case 2:
-      return gu ? run_variant<128, 64, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
-                : run_variant<128, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s);
+      return gu ? run_variant<32, 128, 1, 8, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
+                : (n256 ? run_variant<32, 256, 1, 8, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
+                        : run_variant<32, 128, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s));
     case 3:
-      return gu ? run_variant<128, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 1, s)
-                : (n256 ? run_variant<128, 256, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 1, s)
-                        : run_variant<128, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 1, s));
+      return gu ? run_variant<128, 128, 2, 4, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
+                : (n256 ? run_variant<128, 256, 2, 4, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
+                        : run_variant<128, 128, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s));
     case 4:
-      return gu ? run_variant<64, 64, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s)
-                : run_variant<64, 128, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s);
+      return gu ? run_variant<64, 64, 2, 2, 2, 3>(p, gu, q4, f32out, wgs ? wgs : 3, s)
+                : run_variant<64, 128, 2, 2, 2, 3>(p, gu, q4, f32out, wgs ? wgs : 3, s);
     case 5:
-      return gu ? run_variant<32, 64, 1, 4, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s)
-                : run_variant<32, 128, 1, 4, 2>(p, gu, q4, f32out, wgs ? wgs : 3, s);
+      return gu ? run_variant<32, 128, 1, 4, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
+                : (n256 ? run_variant<32, 256, 1, 4, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
+                        : run_variant<32, 128, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s));
+    case 6:
+      return gu ? run_variant<128, 128, 4, 2, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
+                : (n256 ? run_variant<128, 256, 4, 2, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
+                        : run_variant<128, 128, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s));
     default:
-      return gu ? run_variant<32, 64, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s)
-                : run_variant<32, 128, 1, 4, 1>(p, gu, q4, f32out, wgs ? wgs : 4, s);
+      return gu ? run_variant<128, 64, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
+                : run_variant<128, 128, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s);
   }
 }
 
