@@ -121,7 +121,7 @@ struct Cfg {
   static constexpr int NWAVES = WM * WN, NT = 64 * NWAVES;    // threads per workgroup
   static constexpr int KC = 64;                     // K chunk per LDS stage
   static constexpr int NW = GU ? 2 : 1;             // weight matrices
-  static constexpr int LDK = KC + 8;                // padded LDS row (bf16 elements): 144 bytes
+  static constexpr int LDK = KC;                    // LDS row: 64 bf16 = 128 bytes, 16-byte chunks swizzled
   static constexpr int A_ELEMS = BM * LDK;
   static constexpr int B_ELEMS = NW * BN * LDK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;   // u16 elements per LDS buffer
@@ -139,6 +139,12 @@ struct Cfg {
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
+
+// LDS tiles hold one 128-byte row per A row or weight column (64 consecutive k).  The 16-byte
+// chunk q of row n sits at chunk position q ^ swz(n): the MFMA operand reads (16 consecutive rows,
+// one chunk) are free of bank conflicts and the transposed weight writes are at most 2-way.
+__device__ __forceinline__ int swz(int n) { return ((n >> 1) & 7) ^ ((n >> 4) & 7); }
+__device__ __forceinline__ int lds_off(int n, int q) { return n * 64 + ((q ^ swz(n)) << 3); }
 
 // Registers holding one K chunk in flight: A rows and the weight units of this thread.
 template <class C>
@@ -158,7 +164,8 @@ struct TileCtx {
   __amdgpu_buffer_rsrc_t sr[C::B_UNITS];
   uint32_t b_off[C::B_UNITS];
   uint32_t s_off[C::B_UNITS];
-  int b_lds[C::B_UNITS];
+  int b_row[C::B_UNITS];                            // first LDS row (weight column) of the unit
+  int b_q[C::B_UNITS];                              // 16-byte chunk (dense: 8-byte half in bit 0)
   int nK, row_bytes, s_row_bytes, group_size;
 };
 
@@ -206,7 +213,8 @@ __device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>&
           lo = pack_lo16(ch.b[i][0][d], ch.b[i][1][d]);
           hi = pack_lo16(ch.b[i][2][d], ch.b[i][3][d]);
         }
-        *reinterpret_cast<u32x2*>(sB + t.b_lds[i] + c * C::LDK) = u32x2{lo, hi};
+        const int n = t.b_row[i] + c;
+        *reinterpret_cast<u32x2*>(sB + lds_off(n, t.b_q[i] >> 1) + (t.b_q[i] & 1) * 4) = u32x2{lo, hi};
       }
     } else {
 #pragma unroll
@@ -221,7 +229,7 @@ __device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>&
           const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
           q[h] = pack_bf16x2((float)q0 * sc, (float)q1 * sc);
         }
-        *reinterpret_cast<u32x4*>(sB + t.b_lds[i] + c * C::LDK) = u32x4{q[0], q[1], q[2], q[3]};
+        *reinterpret_cast<u32x4*>(sB + lds_off(t.b_row[i] + c, t.b_q[i])) = u32x4{q[0], q[1], q[2], q[3]};
       }
     }
   }
@@ -239,12 +247,12 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
       bf16x8 av[NM];
 #pragma unroll
       for (int i = 0; i < NM; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(sA + (arow + i * 16) * C::LDK + ks + kofs);
+        av[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(arow + i * 16, (ks + kofs) >> 3));
 #pragma unroll
       for (int m = 0; m < C::NW; ++m)
 #pragma unroll
         for (int j = 0; j < C::NTL; ++j) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + (m * C::BN + bcol + j * 16) * C::LDK + ks + kofs);
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + lds_off(m * C::BN + bcol + j * 16, (ks + kofs) >> 3));
 #pragma unroll
           for (int i = 0; i < NM; ++i)
             acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
@@ -344,7 +352,7 @@ __device__ __forceinline__ void tile_dispatch(int nm, const TileCtx<C>& t, u16* 
 template <class C, typename OutT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD)))
 void k_gemm_bf16(GemmParams p) {
-  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, KC = C::KC, LDK = C::LDK, NT = C::NT;
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, KC = C::KC, NT = C::NT;
   extern __shared__ __attribute__((aligned(16))) u16 smem[];
   u16* buf0 = smem;
   u16* buf1 = smem + (C::STAGES - 1) * C::STAGE;
@@ -389,7 +397,7 @@ void k_gemm_bf16(GemmParams p) {
       int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
       t.a_src[i] = A + (size_t)src * p.K + kc8 * 8;
-      t.a_lds[i] = r * LDK + kc8 * 8;
+      t.a_lds[i] = lds_off(r, kc8);
     }
     // Unit i of a thread reads matrix (tid + NT*i) / per_m, the same for the whole wave.
     constexpr int per_m = KC * BN / 32;
@@ -412,7 +420,8 @@ void k_gemm_bf16(GemmParams p) {
         const int nb = u % (BN / 8), kb = u / (BN / 8);
         const int m = (tid + NT * i) / per_m;
         t.b_off[i] = (uint32_t)((kb * C::R) * p.N + n0 + nb * 8) * 2u;
-        t.b_lds[i] = (m * BN + nb * 8) * LDK + kb * C::R;
+        t.b_row[i] = m * BN + nb * 8;
+        t.b_q[i] = kb;                                   // k-rows 4kb..4kb+3: chunk kb/2, half kb%2
         t.s_off[i] = 0;
       }
     } else {
@@ -425,7 +434,8 @@ void k_gemm_bf16(GemmParams p) {
         const int m = (tid + NT * i) / per_m;
         t.b_off[i] = (uint32_t)(kw * p.N + n0 + nq * 4) * 4u;
         t.s_off[i] = (uint32_t)(n0 + nq * 4) * 2u;
-        t.b_lds[i] = (m * BN + nq * 4) * LDK + kw * 8;
+        t.b_row[i] = m * BN + nq * 4;
+        t.b_q[i] = kw;
       }
     }
     tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0);
@@ -506,6 +516,7 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 
 template <class C, typename OutT>
 hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
+  if (p.N % C::BN != 0) return hipErrorInvalidValue;   // the caller picks a narrower tile
   const size_t lds = C::lds_bytes(p.n_groups);
   // Upper bound of the tile count: every group adds at most one partial m-tile.
   const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
@@ -576,6 +587,9 @@ int env_int(const char* name, int dflt) {
 
 }  // namespace
 
+static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, int wgs,
+                                 hipStream_t s);
+
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   GemmParams p;
   p.a = a.a; p.row_index = a.row_index; p.group_offsets = a.group_offsets;
@@ -595,7 +609,14 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   //   6: 128x128 | 128x256, 8 waves (4x2), 2 buffers, 1/CU
   int v = small_m ? 1 : 2;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
-  const int wgs = env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0);
+  hipError_t err = launch_variant(p, v, gu, q4, f32out, env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0), s);
+  if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrowest tiles
+    err = launch_variant(p, small_m ? 0 : 2, gu, q4, f32out, 0, s);
+  return err;
+}
+
+static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, int wgs,
+                                 hipStream_t s) {
   const bool n256 = p.N % 256 == 0;
   switch (v) {
     case 0:
