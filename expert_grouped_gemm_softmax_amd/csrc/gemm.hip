@@ -235,7 +235,9 @@ __device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>&
   }
 }
 
-// MFMAs of one LDS chunk for the NM live 16-row tiles of this wave.
+// MFMAs of one LDS chunk for the NM live 16-row tiles of this wave (tile i covers rows
+// arow0 - lane%16 + 16 * WM * i: the 16-row tiles of a workgroup tile are dealt to its WM wave
+// rows in turn, which balances partially filled tiles).
 template <class C, int NM>
 __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW][NM > 0 ? NM : 1][C::NTL],
                                               int arow, int bcol, int kofs) {
@@ -247,7 +249,7 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
       bf16x8 av[NM];
 #pragma unroll
       for (int i = 0; i < NM; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(arow + i * 16, (ks + kofs) >> 3));
+        av[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(arow + i * 16 * C::WM, (ks + kofs) >> 3));
 #pragma unroll
       for (int m = 0; m < C::NW; ++m)
 #pragma unroll
@@ -327,7 +329,7 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
     for (int j = 0; j < C::NTL; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wrow0 + i * 16 + (lane >> 4) * 4 + r;
+        const int row = wrow0 + i * 16 * C::WM + (lane >> 4) * 4 + r;
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < rows) {
           float v;
@@ -363,7 +365,7 @@ void k_gemm_bf16(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = p.N / BN;
-  const int wrow0 = wm * (BM / WM), wcol0 = wn * (BN / WN);
+  const int wrow0 = wm * 16, wcol0 = wn * (BN / WN);
 
   build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
   __syncthreads();
@@ -384,7 +386,7 @@ void k_gemm_bf16(GemmParams p) {
     const int row0 = g0 + mt * BM;
     const int rows = min(BM, g1 - row0);
     const int n0 = nt * BN;
-    const int nm = min(C::MT, max(0, (rows - wrow0 + 15) / 16));   // live 16-row tiles of this wave
+    const int nm = min(C::MT, max(0, ((rows + 15) / 16 - wm + WM - 1) / WM));   // live 16-row tiles
 
     TileCtx<C> t;
     t.nK = p.K / KC;
@@ -416,8 +418,11 @@ void k_gemm_bf16(GemmParams p) {
       t.row_bytes = p.N * 2;
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
+        // 16 consecutive lanes take 8 columns x 2 k-row groups, so their transposed LDS writes
+        // hit distinct banks; lanes 0-7 and 16-23 still read 256 contiguous bytes of one row.
         const int u = (tid + NT * i) % per_m;
-        const int nb = u % (BN / 8), kb = u / (BN / 8);
+        constexpr int hi = BN / 64;
+        const int nb = u % 8 + 8 * ((u / 16) % hi), kb = (u / 8) % 2 + 2 * (u / (16 * hi));
         const int m = (tid + NT * i) / per_m;
         t.b_off[i] = (uint32_t)((kb * C::R) * p.N + n0 + nb * 8) * 2u;
         t.b_row[i] = m * BN + nb * 8;
@@ -563,21 +568,20 @@ constexpr bool cfg_ok() {
 }
 
 template <int BM, int BN, int WM, int WN, int ST, int WGS>
-hipError_t run_variant(const GemmParams& p, bool gu, bool q4, bool f32out, int wgs, hipStream_t s) {
-  if (gu) {
-    if constexpr (cfg_ok<BM, BN, WM, WN, true>())
-      return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS>, u16>(p, wgs, s)
-                : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS>, u16>(p, wgs, s);
-    return hipErrorInvalidValue;
-  }
-  if constexpr (cfg_ok<BM, BN, WM, WN, false>()) {
-    if (f32out)
-      return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, float>(p, wgs, s)
-                : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, float>(p, wgs, s);
-    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, u16>(p, wgs, s)
-              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, u16>(p, wgs, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t run_gu(const GemmParams& p, bool q4, int wgs, hipStream_t s) {
+  static_assert(cfg_ok<BM, BN, WM, WN, true>(), "gate/up tile");
+  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS>, u16>(p, wgs ? wgs : WGS, s)
+            : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS>, u16>(p, wgs ? wgs : WGS, s);
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int WGS>
+hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, int wgs, hipStream_t s) {
+  static_assert(cfg_ok<BM, BN, WM, WN, false>(), "down tile");
+  if (f32out)
+    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, float>(p, wgs ? wgs : WGS, s)
+              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, float>(p, wgs ? wgs : WGS, s);
+  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, u16>(p, wgs ? wgs : WGS, s)
+            : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, u16>(p, wgs ? wgs : WGS, s);
 }
 
 int env_int(const char* name, int dflt) {
@@ -601,12 +605,6 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  // Variant ids: rows x columns per tile for gate/up | down, waves per workgroup, LDS buffers,
-  // workgroups per CU.
-  //   0: 32x64 | 32x128,   4 waves, 1 buffer, 4/CU     1: 32x128 | 32x256, 8 waves, 1 buffer, 2/CU
-  //   2: 128x64 | 128x128, 4 waves, 2 buffers, 2/CU    3: 128x128 | 128x256, 8 waves, 2 buffers, 1/CU
-  //   4: 64x64 | 64x128,   4 waves, 2 buffers, 3/CU    5: 32x128 | 32x256, 4 waves, 1 buffer, 2/CU
-  //   6: 128x128 | 128x256, 8 waves (4x2), 2 buffers, 1/CU
   int v = small_m ? 1 : 2;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
   hipError_t err = launch_variant(p, v, gu, q4, f32out, env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0), s);
@@ -617,33 +615,35 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
 
 static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, int wgs,
                                  hipStream_t s) {
+  // Variant ids: rows x columns per tile for gate/up | down, waves per workgroup, LDS buffers,
+  // workgroups per CU.
+  //   0: 32x64 | 32x128,   4 waves, 1 buffer, 4/CU     1: 32x128 | 32x256, 8 waves, 1 buffer, 2/CU
+  //   2: 128x64 | 128x128, 4 waves, 2 buffers, 2/CU    3: 128x128 | 128x256, 8 waves, 2 buffers, 1/CU
+  //   4: 64x64 | 64x128,   4 waves, 2 buffers, 3/CU    5: 32x128 | 32x256, 4 waves, 1 buffer, 2/CU
+  //   6: 128x128 | 128x256, 8 waves (4x2), 2 buffers, 1/CU
+  //   7: 256x64 | 256x128, 4 waves (4x1), 2 buffers, 1/CU
   const bool n256 = p.N % 256 == 0;
+  if (gu) {
+    switch (v) {
+      case 0: return run_gu<32, 64, 1, 4, 1, 4>(p, q4, wgs, s);
+      case 1: return run_gu<32, 128, 1, 8, 1, 2>(p, q4, wgs, s);
+      case 3: return run_gu<128, 128, 2, 4, 2, 1>(p, q4, wgs, s);
+      case 4: return run_gu<64, 64, 2, 2, 2, 3>(p, q4, wgs, s);
+      case 5: return run_gu<32, 128, 1, 4, 1, 2>(p, q4, wgs, s);
+      case 6: return run_gu<128, 128, 4, 2, 2, 1>(p, q4, wgs, s);
+      case 7: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, wgs, s);
+      default: return run_gu<128, 64, 2, 2, 2, 2>(p, q4, wgs, s);
+    }
+  }
   switch (v) {
-    case 0:
-      return gu ? run_variant<32, 64, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s)
-                : run_variant<32, 128, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s);
-    case 1:
-      return gu ? run_variant<32, 128, 1, 8, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
-                : (n256 ? run_variant<32, 256, 1, 8, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
-                        : run_variant<32, 128, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s));
-    case 3:
-      return gu ? run_variant<128, 128, 2, 4, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
-                : (n256 ? run_variant<128, 256, 2, 4, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
-                        : run_variant<128, 128, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s));
-    case 4:
-      return gu ? run_variant<64, 64, 2, 2, 2, 3>(p, gu, q4, f32out, wgs ? wgs : 3, s)
-                : run_variant<64, 128, 2, 2, 2, 3>(p, gu, q4, f32out, wgs ? wgs : 3, s);
-    case 5:
-      return gu ? run_variant<32, 128, 1, 4, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
-                : (n256 ? run_variant<32, 256, 1, 4, 1, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
-                        : run_variant<32, 128, 1, 4, 1, 4>(p, gu, q4, f32out, wgs ? wgs : 4, s));
-    case 6:
-      return gu ? run_variant<128, 128, 4, 2, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
-                : (n256 ? run_variant<128, 256, 4, 2, 2, 1>(p, gu, q4, f32out, wgs ? wgs : 1, s)
-                        : run_variant<128, 128, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s));
-    default:
-      return gu ? run_variant<128, 64, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s)
-                : run_variant<128, 128, 2, 2, 2, 2>(p, gu, q4, f32out, wgs ? wgs : 2, s);
+    case 0: return run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, wgs, s);
+    case 1: return n256 ? run_dn<32, 256, 1, 8, 1, 2>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
+    case 3: return n256 ? run_dn<128, 256, 2, 4, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
+    case 4: return run_dn<64, 128, 2, 2, 2, 3>(p, q4, f32out, wgs, s);
+    case 5: return n256 ? run_dn<32, 256, 1, 4, 1, 2>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
+    case 6: return n256 ? run_dn<128, 256, 4, 2, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
+    case 7: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, wgs, s);
+    default: return run_dn<128, 128, 2, 2, 2, 2>(p, q4, f32out, wgs, s);
   }
 }
 
