@@ -605,11 +605,11 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  int v = small_m ? 1 : 2;
+  int v = small_m ? 5 : 7;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
   hipError_t err = launch_variant(p, v, gu, q4, f32out, env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0), s);
   if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrowest tiles
-    err = launch_variant(p, small_m ? 0 : 2, gu, q4, f32out, 0, s);
+    err = launch_variant(p, small_m ? 0 : 7, gu, q4, f32out, 0, s);
   return err;
 }
 

@@ -34,18 +34,22 @@ __device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
   return same;
 }
 
-// Counts of this wavefront's pairs per local expert, accumulated into mine[0..e_local).
-__device__ __forceinline__ void count_wave(const int32_t* __restrict__ blob, int beg, int end, int e_first,
-                                           int e_local, int nbits, int lane, int32_t* mine) {
-  int le[kSteps];
+// Local expert ids of this wavefront's pairs (-1 outside [0, e_local) or past the end).
+__device__ __forceinline__ void load_local_ids(const int32_t* __restrict__ blob, int beg, int end, int e_first,
+                                               int e_local, int lane, int (&le)[kSteps]) {
 #pragma unroll
   for (int u = 0; u < kSteps; ++u) {
     const int p = beg + 64 * u + lane;
-    le[u] = (p < end) ? blob[p] - e_first : -1;
+    const int id = (p < end) ? blob[min(p, end - 1)] : e_first - 1;
+    le[u] = (id >= e_first && id - e_first < e_local) ? id - e_first : -1;
   }
+}
+
+// Counts of this wavefront's pairs per local expert, accumulated into mine[0..e_local).
+__device__ __forceinline__ void count_wave(const int (&le)[kSteps], int nbits, int lane, int32_t* mine) {
 #pragma unroll
   for (int u = 0; u < kSteps; ++u) {
-    const bool valid = le[u] >= 0 && le[u] < e_local;
+    const bool valid = le[u] >= 0;
     const uint64_t same = match_local(le[u], valid, nbits);
     if (valid && lane == __ffsll((unsigned long long)same) - 1) mine[le[u]] += __popcll(same);
   }
@@ -55,10 +59,12 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
                                                     int e_local, int nbits, int32_t* __restrict__ counts) {
   extern __shared__ int32_t lds[];                         // [4][e_local]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int beg = blockIdx.x * kChunk + wv * kWavePairs;
+  int le[kSteps];
+  load_local_ids(blob, beg, min(P, beg + kWavePairs), e_first, e_local, lane, le);
   for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) lds[i] = 0;
   __syncthreads();
-  const int beg = blockIdx.x * kChunk + wv * kWavePairs;
-  count_wave(blob, beg, min(P, beg + kWavePairs), e_first, e_local, nbits, lane, lds + wv * e_local);
+  count_wave(le, nbits, lane, lds + wv * e_local);
   __syncthreads();
   for (int e = threadIdx.x; e < e_local; e += blockDim.x) {
     int c = 0;
@@ -68,6 +74,9 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
   }
 }
 
+// all_in_lds: the counts of every chunk fit in LDS (loaded with independent, coalesced loads);
+// otherwise each thread walks the chunks of its experts in global memory.
+template <bool ALL_IN_LDS>
 __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ blob, int P, int e_first,
                                                       int e_local, int nbits, int nchunks,
                                                       const int32_t* __restrict__ counts,
@@ -78,14 +87,21 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   int32_t* cnt = lds;                                      // [4][e_local] wave counts -> row bases
   int32_t* base = lds + kWavesPerChunk * e_local;          // [e_local] chunk base per expert
   int32_t* wsum = base + e_local;                          // [4]
+  int32_t* allc = wsum + kWavesPerChunk;                   // [nchunks][e_local] when ALL_IN_LDS
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int chunk = blockIdx.x;
-
-  for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) cnt[i] = 0;
-  __syncthreads();
   const int beg = chunk * kChunk + wv * kWavePairs;
   const int end = min(P, beg + kWavePairs);
-  count_wave(blob, beg, end, e_first, e_local, nbits, lane, cnt + wv * e_local);
+
+  // One round trip: this wavefront's ids and (when they fit) every chunk's counts.
+  int le[kSteps];
+  load_local_ids(blob, beg, end, e_first, e_local, lane, le);
+  if constexpr (ALL_IN_LDS) {
+    for (int i = threadIdx.x; i < nchunks * e_local; i += blockDim.x) allc[i] = counts[i];
+  }
+  for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  count_wave(le, nbits, lane, cnt + wv * e_local);
 
   // Per expert: pairs in earlier chunks and in all chunks; then the offsets (scan over experts).
   int carry = 0;
@@ -93,10 +109,29 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
     const int e = c0 + threadIdx.x;
     int before = 0, total = 0;
     if (e < e_local) {
-      for (int c = 0; c < nchunks; ++c) {
-        const int v = counts[(size_t)c * e_local + e];
-        before += (c < chunk) ? v : 0;
-        total += v;
+      if constexpr (ALL_IN_LDS) {
+        for (int c = 0; c < nchunks; ++c) {
+          const int v = allc[c * e_local + e];
+          before += (c < chunk) ? v : 0;
+          total += v;
+        }
+      } else {
+        int c = 0;
+        for (; c + 8 <= nchunks; c += 8) {
+          int v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = counts[(size_t)(c + u) * e_local + e];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            before += (c + u < chunk) ? v[u] : 0;
+            total += v[u];
+          }
+        }
+        for (; c < nchunks; ++c) {
+          const int v = counts[(size_t)c * e_local + e];
+          before += (c < chunk) ? v : 0;
+          total += v;
+        }
       }
     }
     int incl = total;
@@ -134,16 +169,10 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
 
   int32_t* mine = cnt + wv * e_local;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int le[kSteps];
 #pragma unroll
   for (int u = 0; u < kSteps; ++u) {
     const int p = beg + 64 * u + lane;
-    le[u] = (p < end) ? blob[p] - e_first : -1;
-  }
-#pragma unroll
-  for (int u = 0; u < kSteps; ++u) {
-    const int p = beg + 64 * u + lane;
-    const bool valid = le[u] >= 0 && le[u] < e_local;
+    const bool valid = le[u] >= 0;
     const uint64_t same = match_local(le[u], valid, nbits);
     int row = -1;
     if (valid) row = mine[le[u]] + __popcll(same & below);
@@ -176,8 +205,13 @@ hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t lds_scatter = sizeof(int32_t) * ((kWavesPerChunk + 1) * e_local + kWavesPerChunk);
-  k_perm_scatter<<<dim3(nchunks), dim3(256), lds_scatter, s>>>(blob, P, e_first, e_local, nbits, nchunks,
-                                                               counts, sorted_pairs, group_offsets, pair_pos);
+  const size_t lds_all = sizeof(int32_t) * (size_t)nchunks * e_local;
+  if (lds_scatter + lds_all <= 96 * 1024)
+    k_perm_scatter<true><<<dim3(nchunks), dim3(256), lds_scatter + lds_all, s>>>(
+        blob, P, e_first, e_local, nbits, nchunks, counts, sorted_pairs, group_offsets, pair_pos);
+  else
+    k_perm_scatter<false><<<dim3(nchunks), dim3(256), lds_scatter, s>>>(
+        blob, P, e_first, e_local, nbits, nchunks, counts, sorted_pairs, group_offsets, pair_pos);
   return hipGetLastError();
 }
 

@@ -5,10 +5,10 @@
 // renormalised weight sequence stated in moe.h.  The blob layout follows section 3 (3-to-2
 // all-gather: ids and weight bits stacked on a new leading axis in one int32 array).
 //
-// One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers, and
-// each of the k rounds is a lane-local scan, a 4-step DPP reduction inside each 16-lane row and a
-// comparison of the four row winners read with v_readlane (key: larger logit, then smaller
-// expert id).  The weights need no E-term reduction: slot j's
+// One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers,
+// sorted once per lane; each of the k rounds is a 4-step DPP reduction of the lane heads inside
+// each 16-lane row and a comparison of the four row winners read with v_readlane (key: larger
+// logit, then smaller expert id).  The weights need no E-term reduction: slot j's
 // weight only involves the k selected logits.
 #include "common.h"
 
@@ -69,26 +69,31 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                     // uniform per wave
   const float* row = logits + (size_t)t * E;
+  // Lane l owns experts l, l+64, ...; its list is sorted once by the selection key, so each round
+  // only compares the heads of the 64 lists and the winning lane drops its head.
   float v[PER_LANE];
-  uint32_t avail = 0;
+  int id[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
     v[i] = 0.0f;
-    if (e < E) { v[i] = __builtin_nontemporal_load(row + e); avail |= 1u << i; }
+    id[i] = kNone;
+    if (e < E) { v[i] = __builtin_nontemporal_load(row + e); id[i] = e; }
   }
+#pragma unroll
+  for (int i = 1; i < PER_LANE; ++i)                      // insertion sort, fully unrolled
+#pragma unroll
+    for (int j = i; j > 0; --j)
+      if (beats(v[j], id[j], v[j - 1], id[j - 1])) {
+        const float tv = v[j]; v[j] = v[j - 1]; v[j - 1] = tv;
+        const int ti = id[j]; id[j] = id[j - 1]; id[j - 1] = ti;
+      }
   float sel_v = 0.0f;   // slot `lane` (lanes < k)
   int sel_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int bid = kNone;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i)
-      if ((avail >> i) & 1u) {
-        const int e = lane + 64 * i;
-        if (beats(v[i], e, bv, bid)) { bv = v[i]; bid = e; }
-      }
-    // best of each 16-lane row, in every lane of that row
+    float bv = v[0];
+    int bid = id[0];
+    // best head of each 16-lane row, in every lane of that row
     dpp_step<kQuadXor1>(bv, bid);
     dpp_step<kQuadXor2>(bv, bid);
     dpp_step<kRowHalfMirror>(bv, bid);
@@ -102,7 +107,12 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
       const int rid = __builtin_amdgcn_readlane(bid, r);
       if (beats(rv, rid, wv, wid)) { wv = rv; wid = rid; }
     }
-    if (lane == (wid & 63)) avail &= ~(1u << (wid >> 6));
+    if (lane == (wid & 63)) {                             // the winner's list advances
+#pragma unroll
+      for (int i = 0; i + 1 < PER_LANE; ++i) { v[i] = v[i + 1]; id[i] = id[i + 1]; }
+      v[PER_LANE - 1] = 0.0f;
+      id[PER_LANE - 1] = kNone;
+    }
     if (lane == j) { sel_v = wv; sel_id = wid; }
   }
   const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
