@@ -112,8 +112,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1, int REGSETS_ = 2>
 struct Cfg {
+  // Chunks held in registers between their loads and their LDS stores (two LDS buffers only).
+  static constexpr int REGSETS = REGSETS_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr int WGS = WGS_;                  // intended workgroups per CU
   static constexpr int WAVES_PER_SIMD = (WM_ * WN_ * WGS_ + 3) / 4;   // register budget target
@@ -131,9 +133,13 @@ struct Cfg {
   static constexpr int B_UNITS = NW * KC * BN / 32 / NT;
   static constexpr int R = 4;                       // dense: k-rows per transposed block
   static constexpr int MT = BM / WM / 16;           // 16-row MFMA tiles per wave
+  // Wide wave tiles: keep the scheduler from hoisting the next k-step's operand reads (their
+  // registers would not fit beside the accumulators).
+  static constexpr bool SCHED_SPLIT = (BM / WM) * (BN / WN) * (GU ? 2 : 1) >= 64 * 256;
   static constexpr int NTL = BN / WN / 16;          // 16-column MFMA tiles per wave and matrix
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves");
   static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
+  static_assert(REGSETS == 2 || (REGSETS == 1 && STAGES == 2), "register sets");
   static_assert(A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0, "A tile split");
   static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * NT) == 0, "B tile split");
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
@@ -146,12 +152,21 @@ struct Cfg {
 __device__ __forceinline__ int swz(int n) { return ((n >> 1) & 7) ^ ((n >> 4) & 7); }
 __device__ __forceinline__ int lds_off(int n, int q) { return n * 64 + ((q ^ swz(n)) << 3); }
 
-// Registers holding one K chunk in flight: A rows and the weight units of this thread.
+// Registers holding one K chunk in flight: the activation rows and the weight units of this
+// thread.
 template <class C>
-struct Chunk {
+struct AChunk {
   u32x4 a[C::A_LOADS];
+};
+template <class C>
+struct WChunk {
   u32x4 b[C::B_UNITS][C::Q4 ? 1 : C::R];
   u32x2 s[C::B_UNITS];
+};
+template <class C>
+struct Chunk {
+  AChunk<C> a;
+  WChunk<C> w;
 };
 
 // Everything a thread needs to move one tile's chunks: gathered A row pointers, the weight and
@@ -169,13 +184,19 @@ struct TileCtx {
   int nK, row_bytes, s_row_bytes, group_size;
 };
 
+// Loads are unconditional (indices clamped to the last chunk): a branch around a load would make
+// the compiler wait for every outstanding load, including the chunks prefetched ahead.
 template <class C>
-__device__ __forceinline__ void load_chunk(const TileCtx<C>& t, int kc, Chunk<C>& ch) {
-  kc = min(kc, t.nK - 1);                           // unconditional loads: a branch around a load
-                                                    // would make the compiler drain the prefetch
+__device__ __forceinline__ void load_a(const TileCtx<C>& t, int kc, AChunk<C>& ch) {
+  kc = min(kc, t.nK - 1);
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i)
     ch.a[i] = *reinterpret_cast<const u32x4*>(t.a_src[i] + (size_t)kc * C::KC);
+}
+
+template <class C>
+__device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& ch) {
+  kc = min(kc, t.nK - 1);
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (!C::Q4) {
@@ -193,11 +214,15 @@ __device__ __forceinline__ void load_chunk(const TileCtx<C>& t, int kc, Chunk<C>
 }
 
 template <class C>
-__device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>& ch, u16* buf) {
+__device__ __forceinline__ void store_a(const TileCtx<C>& t, const AChunk<C>& ch, u16* buf) {
   u16* sA = buf;
-  u16* sB = buf + C::A_ELEMS;
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + t.a_lds[i]) = ch.a[i];
+}
+
+template <class C>
+__device__ __forceinline__ void store_w(const TileCtx<C>& t, const WChunk<C>& ch, u16* buf) {
+  u16* sB = buf + C::A_ELEMS;
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (!C::Q4) {
@@ -235,6 +260,18 @@ __device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>&
   }
 }
 
+template <class C>
+__device__ __forceinline__ void load_chunk(const TileCtx<C>& t, int kc, Chunk<C>& ch) {
+  load_a(t, kc, ch.a);
+  load_w(t, kc, ch.w);
+}
+
+template <class C>
+__device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>& ch, u16* buf) {
+  store_a(t, ch.a, buf);
+  store_w(t, ch.w, buf);
+}
+
 // MFMAs of one LDS chunk for the NM live 16-row tiles of this wave (tile i covers rows
 // arow0 - lane%16 + 16 * WM * i: the 16-row tiles of a workgroup tile are dealt to its WM wave
 // rows in turn, which balances partially filled tiles).
@@ -259,6 +296,7 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
           for (int i = 0; i < NM; ++i)
             acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
         }
+      if constexpr (C::SCHED_SPLIT) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -282,11 +320,30 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
 
   // Loads run two chunks ahead of the MFMAs (two register sets).  With two LDS buffers one
   // barrier per chunk suffices; with one buffer it is refilled between two barriers.
-  Chunk<C> c0, c1;
-  load_chunk(t, 0, c0);
-  load_chunk(t, 1, c1);
   int kc = 0;
-  if constexpr (C::STAGES == 2) {
+  if constexpr (C::STAGES == 2 && C::REGSETS == 1) {
+    // One register set: a chunk's loads are issued right after the previous chunk is stored and
+    // have one chunk of MFMAs (and the other waves of the SIMD) to arrive.
+    Chunk<C> c0;
+    load_chunk(t, 0, c0);
+    store_chunk(t, c0, buf0);
+    load_chunk(t, 1, c0);
+    __syncthreads();
+    for (; kc + 1 < nK; kc += 2) {
+      compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+      store_chunk(t, c0, buf1);
+      load_chunk(t, kc + 2, c0);
+      __syncthreads();
+      compute_chunk<C, NM>(buf1, acc, arow, bcol, kofs);
+      store_chunk(t, c0, buf0);
+      load_chunk(t, kc + 3, c0);
+      __syncthreads();
+    }
+    if (kc < nK) compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+  } else if constexpr (C::STAGES == 2) {
+    Chunk<C> c0, c1;
+    load_chunk(t, 0, c0);
+    load_chunk(t, 1, c1);
     store_chunk(t, c0, buf0);
     load_chunk(t, 2, c0);
     __syncthreads();
@@ -302,16 +359,21 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
     }
     if (kc < nK) compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
   } else {
+    Chunk<C> c0, c1;
+    load_chunk(t, 0, c0);
+    load_chunk(t, 1, c1);
+    // The next loads are issued after the MFMAs: when the vector L1 has no room for more misses
+    // a load blocks the wave at issue, and it must not hold back the MFMAs.
     for (; kc + 1 < nK; kc += 2) {
       store_chunk(t, c0, buf0);
       __syncthreads();
-      load_chunk(t, kc + 2, c0);
       compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+      load_chunk(t, kc + 2, c0);
       __syncthreads();
       store_chunk(t, c1, buf0);
       __syncthreads();
-      load_chunk(t, kc + 3, c1);
       compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+      load_chunk(t, kc + 3, c1);
       __syncthreads();
     }
     if (kc < nK) {
@@ -382,7 +444,12 @@ void k_gemm_bf16(GemmParams p) {
     const int g0 = s_goff[e], g1 = s_goff[e + 1];
     const int mtiles = (g1 - g0 + BM - 1) / BM;
     const int local = tile - s_tstart[e];
-    const int mt = local % mtiles, nt = local / mtiles;
+    // Inside an expert, tiles go in groups of up to kGroupM m-tiles x all n-tiles, m-tile fastest:
+    // the workgroups of one XCD then share a few activation tiles and a few weight slabs in L2.
+    constexpr int kGroupM = 4;
+    const int grp = local / (kGroupM * tiles_n), in_grp = local % (kGroupM * tiles_n);
+    const int gm = min(kGroupM, mtiles - grp * kGroupM);
+    const int mt = grp * kGroupM + in_grp % gm, nt = in_grp / gm;
     const int row0 = g0 + mt * BM;
     const int rows = min(BM, g1 - row0);
     const int n0 = nt * BN;
@@ -567,21 +634,21 @@ constexpr bool cfg_ok() {
          (A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0) && BM / WM >= 16 && BN / WN >= 16;
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int WGS>
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
 hipError_t run_gu(const GemmParams& p, bool q4, int wgs, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, true>(), "gate/up tile");
-  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS>, u16>(p, wgs ? wgs : WGS, s)
-            : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS>, u16>(p, wgs ? wgs : WGS, s);
+  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>, u16>(p, wgs ? wgs : WGS, s)
+            : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS, RS>, u16>(p, wgs ? wgs : WGS, s);
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int WGS>
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
 hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, int wgs, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, false>(), "down tile");
   if (f32out)
-    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, float>(p, wgs ? wgs : WGS, s)
-              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, float>(p, wgs ? wgs : WGS, s);
-  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS>, u16>(p, wgs ? wgs : WGS, s)
-            : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS>, u16>(p, wgs ? wgs : WGS, s);
+    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, float>(p, wgs ? wgs : WGS, s)
+              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, float>(p, wgs ? wgs : WGS, s);
+  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, u16>(p, wgs ? wgs : WGS, s)
+            : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, u16>(p, wgs ? wgs : WGS, s);
 }
 
 int env_int(const char* name, int dflt) {
@@ -605,11 +672,11 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  int v = small_m ? 5 : 7;
+  int v = small_m ? 5 : 8;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
   hipError_t err = launch_variant(p, v, gu, q4, f32out, env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0), s);
   if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrowest tiles
-    err = launch_variant(p, small_m ? 0 : 7, gu, q4, f32out, 0, s);
+    err = launch_variant(p, small_m ? 0 : 8, gu, q4, f32out, 0, s);
   return err;
 }
 
@@ -621,7 +688,9 @@ static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, b
   //   2: 128x64 | 128x128, 4 waves, 2 buffers, 2/CU    3: 128x128 | 128x256, 8 waves, 2 buffers, 1/CU
   //   4: 64x64 | 64x128,   4 waves, 2 buffers, 3/CU    5: 32x128 | 32x256, 4 waves, 1 buffer, 2/CU
   //   6: 128x128 | 128x256, 8 waves (4x2), 2 buffers, 1/CU
-  //   7: 256x64 | 256x128, 4 waves (4x1), 2 buffers, 1/CU
+  //   7: 256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU, one chunk in registers
+  //   8: 256x64 | 256x128, 4 waves (4x1), 2 buffers, 1/CU
+  //   9: 256x128 | 256x256, 4 waves (4x1), 2 buffers, 1/CU
   const bool n256 = p.N % 256 == 0;
   if (gu) {
     switch (v) {
@@ -631,7 +700,9 @@ static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, b
       case 4: return run_gu<64, 64, 2, 2, 2, 3>(p, q4, wgs, s);
       case 5: return run_gu<32, 128, 1, 4, 1, 2>(p, q4, wgs, s);
       case 6: return run_gu<128, 128, 4, 2, 2, 1>(p, q4, wgs, s);
-      case 7: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, wgs, s);
+      case 7: return run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, wgs, s);
+      case 8: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, wgs, s);
+      case 9: return run_gu<256, 128, 4, 1, 2, 1>(p, q4, wgs, s);
       default: return run_gu<128, 64, 2, 2, 2, 2>(p, q4, wgs, s);
     }
   }
@@ -642,7 +713,9 @@ static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, b
     case 4: return run_dn<64, 128, 2, 2, 2, 3>(p, q4, f32out, wgs, s);
     case 5: return n256 ? run_dn<32, 256, 1, 4, 1, 2>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
     case 6: return n256 ? run_dn<128, 256, 4, 2, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    case 7: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, wgs, s);
+    case 7: return n256 ? run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
+    case 8: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, wgs, s);
+    case 9: return n256 ? run_dn<256, 256, 4, 1, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
     default: return run_dn<128, 128, 2, 2, 2, 2>(p, q4, f32out, wgs, s);
   }
 }
