@@ -16,14 +16,15 @@
 //    cut into 8 contiguous ranges and XCD x's workgroups walk range x, so tiles sharing a weight
 //    slab or activation rows share one L2.
 //  - Activation rows are gathered (row_index / row_div) straight into LDS, 16 bytes per lane.
-//  - Dense bf16 weights W[e][K][N] are N-contiguous while MFMA wants 8 consecutive k per lane: each
-//    lane loads an R x 8 block (R k-rows, 16 bytes each), transposes it in registers with v_perm
-//    and writes it K-contiguous into LDS ([n][k], padded rows).  int4 words already hold 8
-//    consecutive k of one column: they are dequantised (q * scale, rounded to bf16) straight
-//    into the same [n][k] LDS layout.
+//  - Activation rows and dense weight rows (W[e][n][k], K-contiguous like a linear layer's
+//    weight) are copied into LDS the same way: 16 bytes per lane, 8 lanes per 128-byte row chunk,
+//    giving [row][k] tiles whose rows are what the MFMA operands read (8 consecutive k per lane).
+//    int4 words [e][k/8][n] hold 8 consecutive k of one column: they are dequantised
+//    (q * scale, rounded to bf16) into the same [n][k] LDS layout.
 //  - v_mfma_f32_16x16x32_bf16 with fp32 accumulators; SwiGLU fused in the epilogue (each lane
 //    holds the gate and the up value of the same output element).
-//  - Global loads for chunk c+1 are issued before the MFMAs of chunk c (register prefetch).
+//  - Global loads run ahead of the MFMAs through registers (one or two chunks) and one or two
+//    LDS buffers.
 #include <cstdlib>
 
 #include "common.h"
@@ -131,11 +132,11 @@ struct Cfg {
   static constexpr int A_LOADS = A_CHUNKS >= NT ? A_CHUNKS / NT : 1;   // per thread (small tiles: duplicated)
   // B units per thread: a dense R x 8 block or one 16-byte row of 4 int4 words, 32 weights each
   static constexpr int B_UNITS = NW * KC * BN / 32 / NT;
-  static constexpr int R = 4;                       // dense: k-rows per transposed block
+  static constexpr int R = 4;                       // dense: 16-byte pieces per unit
+  static constexpr int B_PIECES = B_UNITS * R;      // dense: 16-byte pieces per thread
+  static constexpr int SLICE_ROWS = NT / 8;         // 128-byte rows filled by one 16-byte piece per thread
+  static constexpr int NRSRC = B_UNITS > NW ? B_UNITS : NW;
   static constexpr int MT = BM / WM / 16;           // 16-row MFMA tiles per wave
-  // Wide wave tiles: keep the scheduler from hoisting the next k-step's operand reads (their
-  // registers would not fit beside the accumulators).
-  static constexpr bool SCHED_SPLIT = (BM / WM) * (BN / WN) * (GU ? 2 : 1) >= 64 * 256;
   static constexpr int NTL = BN / WN / 16;          // 16-column MFMA tiles per wave and matrix
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves");
   static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
@@ -143,14 +144,21 @@ struct Cfg {
   static_assert(A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0, "A tile split");
   static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * NT) == 0, "B tile split");
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
+  static_assert(Q4 || BN % SLICE_ROWS == 0, "a dense piece slice stays inside one weight matrix");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
 
-// LDS tiles hold one 128-byte row per A row or weight column (64 consecutive k).  The 16-byte
-// chunk q of row n sits at chunk position q ^ swz(n): the MFMA operand reads (16 consecutive rows,
-// one chunk) are free of bank conflicts and the transposed weight writes are at most 2-way.
-__device__ __forceinline__ int swz(int n) { return ((n >> 1) & 7) ^ ((n >> 4) & 7); }
-__device__ __forceinline__ int lds_off(int n, int q) { return n * 64 + ((q ^ swz(n)) << 3); }
+// LDS tiles hold one 128-byte row (64 consecutive k) per activation row or weight column, in
+// 16-byte chunks; chunk q of row n sits at position q ^ swz(n).  The MFMA operand reads (16
+// consecutive rows, one chunk per 16-lane group) are free of bank conflicts because swz runs over
+// 0..7 on the even and on the odd rows of every 16-row block.  Activation tiles and dense weight
+// tiles use swz(n) = (n/2) mod 8, a function of n mod 16 only: all operand reads and row writes
+// of a lane are then one base register plus immediate offsets.  int4 weight tiles also XOR in
+// (n/16) mod 8, which keeps their dequantised column writes at most 2-way conflicted.
+__device__ __forceinline__ int lds_off_rows(int n, int q) { return n * 64 + ((q ^ ((n >> 1) & 7)) << 3); }
+__device__ __forceinline__ int lds_off_q4(int n, int q) {
+  return n * 64 + ((q ^ ((n >> 1) & 7) ^ ((n >> 4) & 7)) << 3);
+}
 
 // Registers holding one K chunk in flight: the activation rows and the weight units of this
 // thread.
@@ -173,14 +181,18 @@ struct Chunk {
 // scale descriptors of the tile's expert and its own byte offsets, and LDS destinations.
 template <class C>
 struct TileCtx {
-  const u16* a_src[C::A_LOADS];
-  int a_lds[C::A_LOADS];
-  __amdgpu_buffer_rsrc_t wr[C::B_UNITS];          // descriptor of the matrix each unit reads
+  __amdgpu_buffer_rsrc_t ar;                        // activation matrix
+  uint32_t a_off[C::A_LOADS];                       // byte offset of the lane's piece of chunk 0
+  int a_lds;                                        // LDS destination of the lane's first piece
+  __amdgpu_buffer_rsrc_t wr[C::NRSRC];           // dense: one per matrix; int4: one per unit
   __amdgpu_buffer_rsrc_t sr[C::B_UNITS];
-  uint32_t b_off[C::B_UNITS];
-  uint32_t s_off[C::B_UNITS];
-  int b_row[C::B_UNITS];                            // first LDS row (weight column) of the unit
-  int b_q[C::B_UNITS];                              // 16-byte chunk (dense: 8-byte half in bit 0)
+  uint32_t b_voff;                                  // dense: lane offset (row lane/8, chunk lane%8)
+  uint32_t b_soff;                                  // dense: wave-uniform offset of the wave's rows
+  int b_lds;                                        // dense: LDS destination of the lane's first piece
+  uint32_t b_off[C::B_UNITS];                       // int4: word offset of the unit
+  uint32_t s_off[C::B_UNITS];                       // int4: scale offset of the unit
+  int b_row[C::B_UNITS];                            // int4: first LDS row (weight column) of the unit
+  int b_q[C::B_UNITS];                              // int4: 16-byte chunk of the unit
   int nK, row_bytes, s_row_bytes, group_size;
 };
 
@@ -191,7 +203,7 @@ __device__ __forceinline__ void load_a(const TileCtx<C>& t, int kc, AChunk<C>& c
   kc = min(kc, t.nK - 1);
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i)
-    ch.a[i] = *reinterpret_cast<const u32x4*>(t.a_src[i] + (size_t)kc * C::KC);
+    ch.a[i] = __builtin_amdgcn_raw_buffer_load_b128(t.ar, t.a_off[i], (uint32_t)kc * (C::KC * 2), 0);
 }
 
 template <class C>
@@ -200,10 +212,14 @@ __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& c
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (!C::Q4) {
+      // piece x = i*R + r covers weight rows SLICE_ROWS*x .. SLICE_ROWS*(x+1)-1 of the NW*BN tile rows
 #pragma unroll
-      for (int r = 0; r < C::R; ++r)
-        ch.b[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
-            t.wr[i], t.b_off[i] + (uint32_t)(kc * C::KC + r) * t.row_bytes, 0, 2 /* nontemporal */);
+      for (int r = 0; r < C::R; ++r) {
+        const int x = i * C::R + r;
+        const int rows_x = C::SLICE_ROWS * x;
+        const uint32_t so = t.b_soff + (uint32_t)(rows_x % C::BN) * t.row_bytes + (uint32_t)kc * (C::KC * 2);
+        ch.b[i][r] = __builtin_amdgcn_raw_buffer_load_b128(t.wr[rows_x / C::BN], t.b_voff, so, 2 /* nontemporal */);
+      }
     } else {
       ch.b[i][0] = __builtin_amdgcn_raw_buffer_load_b128(
           t.wr[i], t.b_off[i] + (uint32_t)(kc * (C::KC / 8)) * t.row_bytes, 0, 2);
@@ -217,7 +233,7 @@ template <class C>
 __device__ __forceinline__ void store_a(const TileCtx<C>& t, const AChunk<C>& ch, u16* buf) {
   u16* sA = buf;
 #pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + t.a_lds[i]) = ch.a[i];
+  for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + t.a_lds + C::SLICE_ROWS * i * 64) = ch.a[i];
 }
 
 template <class C>
@@ -226,21 +242,9 @@ __device__ __forceinline__ void store_w(const TileCtx<C>& t, const WChunk<C>& ch
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (!C::Q4) {
-      // ch.b[i][r] = k-row r, dword d = columns (2d, 2d+1); column c gets k-rows 0..3.
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int d = c >> 1;
-        uint32_t lo, hi;
-        if (c & 1) {
-          lo = pack_hi16(ch.b[i][0][d], ch.b[i][1][d]);
-          hi = pack_hi16(ch.b[i][2][d], ch.b[i][3][d]);
-        } else {
-          lo = pack_lo16(ch.b[i][0][d], ch.b[i][1][d]);
-          hi = pack_lo16(ch.b[i][2][d], ch.b[i][3][d]);
-        }
-        const int n = t.b_row[i] + c;
-        *reinterpret_cast<u32x2*>(sB + lds_off(n, t.b_q[i] >> 1) + (t.b_q[i] & 1) * 4) = u32x2{lo, hi};
-      }
+      for (int r = 0; r < C::R; ++r)
+        *reinterpret_cast<u32x4*>(sB + t.b_lds + C::SLICE_ROWS * (i * C::R + r) * 64) = ch.b[i][r];
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -254,7 +258,7 @@ __device__ __forceinline__ void store_w(const TileCtx<C>& t, const WChunk<C>& ch
           const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
           q[h] = pack_bf16x2((float)q0 * sc, (float)q1 * sc);
         }
-        *reinterpret_cast<u32x4*>(sB + lds_off(t.b_row[i] + c, t.b_q[i])) = u32x4{q[0], q[1], q[2], q[3]};
+        *reinterpret_cast<u32x4*>(sB + lds_off_q4(t.b_row[i] + c, t.b_q[i])) = u32x4{q[0], q[1], q[2], q[3]};
       }
     }
   }
@@ -285,18 +289,21 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
     for (int ks = 0; ks < C::KC; ks += 32) {
       bf16x8 av[NM];
 #pragma unroll
-      for (int i = 0; i < NM; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(arow + i * 16 * C::WM, (ks + kofs) >> 3));
+      for (int i = 0; i < NM; ++i) {
+        const int off = lds_off_rows(arow, (ks + kofs) >> 3) + i * 16 * C::WM * 64;
+        av[i] = *reinterpret_cast<const bf16x8*>(sA + off);
+      }
 #pragma unroll
       for (int m = 0; m < C::NW; ++m)
 #pragma unroll
         for (int j = 0; j < C::NTL; ++j) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + lds_off(m * C::BN + bcol + j * 16, (ks + kofs) >> 3));
+          const int off = C::Q4 ? lds_off_q4(m * C::BN + bcol + j * 16, (ks + kofs) >> 3)
+                                : lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64;
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + off);
 #pragma unroll
           for (int i = 0; i < NM; ++i)
             acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
         }
-      if constexpr (C::SCHED_SPLIT) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -434,7 +441,8 @@ void k_gemm_bf16(GemmParams p) {
   const int total = s_tstart[p.n_groups];
   const TileIter it = tile_range(total);
 
-  const u16* A = static_cast<const u16*>(p.a);
+  // the host checks a_rows * K * 2 < 2^32
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, (uint32_t)((size_t)p.a_rows * p.K * 2));
   OutT* O = static_cast<OutT*>(p.out);
   const uint32_t w_bytes = C::Q4 ? (uint32_t)((size_t)p.K / 8 * p.N * 4) : (uint32_t)((size_t)p.K * p.N * 2);
   const uint32_t s_bytes = C::Q4 ? (uint32_t)((size_t)(p.K / p.group_size) * p.N * 2) : 0u;
@@ -456,6 +464,7 @@ void k_gemm_bf16(GemmParams p) {
     const int nm = min(C::MT, max(0, ((rows + 15) / 16 - wm + WM - 1) / WM));   // live 16-row tiles
 
     TileCtx<C> t;
+    t.ar = a_rsrc;
     t.nK = p.K / KC;
     t.group_size = p.group_size;
 #pragma unroll
@@ -465,38 +474,31 @@ void k_gemm_bf16(GemmParams p) {
       const int rr = row0 + min(r, rows - 1);          // padding rows repeat the last valid row
       int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
-      t.a_src[i] = A + (size_t)src * p.K + kc8 * 8;
-      t.a_lds[i] = lds_off(r, kc8);
+      t.a_off[i] = (uint32_t)(((size_t)src * p.K + kc8 * 8) * 2);
     }
-    // Unit i of a thread reads matrix (tid + NT*i) / per_m, the same for the whole wave.
-    constexpr int per_m = KC * BN / 32;
-    static_assert(per_m % 64 == 0, "a wave's units read one matrix");
-#pragma unroll
-    for (int i = 0; i < C::B_UNITS; ++i) {
-      const int m = __builtin_amdgcn_readfirstlane((tid + NT * i) / per_m);
-      const char* W = static_cast<const char*>(m == 0 ? p.w0 : p.w1);
-      t.wr[i] = make_rsrc(W + (size_t)e * w_bytes, w_bytes);
-      if constexpr (C::Q4) {
-        const char* S = static_cast<const char*>(m == 0 ? p.s0 : p.s1);
-        t.sr[i] = make_rsrc(S + (size_t)e * s_bytes, s_bytes);
-      }
-    }
+    // piece i of a thread lands SLICE_ROWS * i rows below piece 0 (the swizzle repeats every 16 rows)
+    t.a_lds = lds_off_rows((tid % C::A_CHUNKS) / (KC / 8), tid % (KC / 8));
     if constexpr (!C::Q4) {
-      t.row_bytes = p.N * 2;
+      // Weight rows are K-contiguous ([e][n][k]) and go to LDS like activation rows: 8 lanes per
+      // 128-byte row chunk, wave w's lanes on rows 8w .. 8w+7 of every slice of SLICE_ROWS rows.
+#pragma unroll
+      for (int m = 0; m < C::NW; ++m)
+        t.wr[m] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)e * w_bytes, w_bytes);
+      t.row_bytes = p.K * 2;
+      t.b_voff = (uint32_t)((lane >> 3) * t.row_bytes + (lane & 7) * 16);
+      t.b_soff = (uint32_t)((n0 + wave * 8) * t.row_bytes);
+      t.b_lds = lds_off_rows(wave * 8 + (lane >> 3), lane & 7);
+    } else {
+      // Unit i of a thread (one 16-byte row piece: 4 words of 8 k each) reads matrix
+      // (tid + NT*i) / per_m, the same for the whole wave.
+      constexpr int per_m = KC * BN / 32;
+      static_assert(per_m % 64 == 0, "a wave's units read one matrix");
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
-        // 16 consecutive lanes take 8 columns x 2 k-row groups, so their transposed LDS writes
-        // hit distinct banks; lanes 0-7 and 16-23 still read 256 contiguous bytes of one row.
-        const int u = (tid + NT * i) % per_m;
-        constexpr int hi = BN / 64;
-        const int nb = u % 8 + 8 * ((u / 16) % hi), kb = (u / 8) % 2 + 2 * (u / (16 * hi));
-        const int m = (tid + NT * i) / per_m;
-        t.b_off[i] = (uint32_t)((kb * C::R) * p.N + n0 + nb * 8) * 2u;
-        t.b_row[i] = m * BN + nb * 8;
-        t.b_q[i] = kb;                                   // k-rows 4kb..4kb+3: chunk kb/2, half kb%2
-        t.s_off[i] = 0;
+        const int m = __builtin_amdgcn_readfirstlane((tid + NT * i) / per_m);
+        t.wr[i] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)e * w_bytes, w_bytes);
+        t.sr[i] = make_rsrc(static_cast<const char*>(m == 0 ? p.s0 : p.s1) + (size_t)e * s_bytes, s_bytes);
       }
-    } else {
       t.row_bytes = p.N * 4;
       t.s_row_bytes = p.N * 2;
 #pragma unroll
@@ -521,7 +523,7 @@ template <bool GU>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
   constexpr int BM = 32, BN = 64, KC = 32, NW = GU ? 2 : 1;
   __shared__ float sA[BM][KC + 1];
-  __shared__ float sB[NW][KC][BN];
+  __shared__ float sB[NW][BN][KC + 1];             // weight rows [n][k], padded
   extern __shared__ int tbl[];
   int* s_tstart = tbl;
   int* s_goff = tbl + (p.n_groups + 1);
@@ -551,9 +553,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
         sA[r][kk] = A[(size_t)src * p.K + k0 + kk];
       }
       for (int i = tid; i < NW * KC * BN; i += 256) {
-        const int m = i / (KC * BN), v = i % (KC * BN), kk = v / BN, n = v % BN;
+        const int m = i / (KC * BN), v = i % (KC * BN), n = v / KC, kk = v % KC;
         const float* W = static_cast<const float*>(m == 0 ? p.w0 : p.w1);
-        sB[m][kk][n] = W[((size_t)e * p.K + k0 + kk) * p.N + n0 + n];
+        sB[m][n][kk] = W[((size_t)e * p.N + n0 + n) * p.K + k0 + kk];
       }
       __syncthreads();
       for (int kk = 0; kk < KC; ++kk) {
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
         for (int m = 0; m < NW; ++m)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const float b = sB[m][kk][tx + 16 * c];
+            const float b = sB[m][tx + 16 * c][kk];
             acc[m][0][c] = fmaf(a0, b, acc[m][0][c]);
             acc[m][1][c] = fmaf(a1, b, acc[m][1][c]);
           }
@@ -617,14 +619,10 @@ hipError_t run_f32(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Tile variants.  Decode-shaped calls (few rows per expert) stream weights with 32-row tiles and
-// many workgroups per CU; prefill-shaped calls use 128-row tiles.  MOE_GEMM_VARIANT (debug only)
-// forces one variant index for tuning sweeps.
+// Tile variants.  Decode-shaped calls (few rows per expert) stream weights with 32-row tiles, four
+// workgroups per CU; prefill-shaped calls use 256-row tiles of 8 waves, one workgroup per CU.
+// MOE_GEMM_VARIANT_GU / _DN (tuning sweeps only) force a variant index.
 namespace {
-
-struct Variant {
-  int bm, bn, wgs_per_cu;
-};
 
 // Whether a tile shape splits evenly over its workgroup (mirrors the static checks of Cfg).
 template <int BM, int BN, int WM, int WN, bool GU>
@@ -672,7 +670,7 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  int v = small_m ? 5 : 8;
+  int v = small_m ? 0 : 7;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
   hipError_t err = launch_variant(p, v, gu, q4, f32out, env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0), s);
   if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrowest tiles

@@ -15,9 +15,11 @@ from . import _abi, ops
 class ExpertWeights:
     """Device-resident weights of the local experts (and of the optional shared expert).
 
-    Dense: w_gate, w_up [e_local][H][I], w_down [e_local][I][H] in the activation dtype.
-    int4:  int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N].
-    Shared expert (dense, activation dtype): gate, up [H][Is], down [Is][H]."""
+    Dense ([out][in], the orientation of a linear layer's weight): w_gate, w_up [e_local][I][H],
+    w_down [e_local][H][I] in the activation dtype.
+    int4:  int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N]
+    (K = in, N = out).
+    Shared expert (dense, activation dtype): gate, up [Is][H], down [H][Is]."""
     w_gate: torch.Tensor
     w_up: torch.Tensor
     w_down: torch.Tensor
@@ -88,8 +90,23 @@ class MoELayer:
         # every row would add an error proportional to |y| on top of the bf16 GEMM operands.
         self.o_dtype = torch.float32
         self.y_dtype = y_dtype
-        self.shared_I = 0 if weights.shared_gate is None else weights.shared_gate.shape[1]
+        self.shared_I = 0 if weights.shared_gate is None else weights.shared_gate.shape[0]
+        self._check_shapes()
         self._buf: dict[int, Buffers] = {}
+
+    def _check_shapes(self):
+        W, H, I, el = self.weights, self.H, self.I, self.e_local
+        if W.int4:
+            want = {"w_gate": (el, H // 8, I), "w_up": (el, H // 8, I), "w_down": (el, I // 8, H)}
+        else:
+            want = {"w_gate": (el, I, H), "w_up": (el, I, H), "w_down": (el, H, I)}
+        if self.shared_I:
+            Is = self.shared_I
+            want.update(shared_gate=(Is, H), shared_up=(Is, H), shared_down=(H, Is))
+        for name, shape in want.items():
+            got = tuple(getattr(W, name).shape)
+            if got != shape:
+                raise ValueError(f"{name}: shape {got}, expected {shape}")
 
     @classmethod
     def from_config(cls, cfg, weights: ExpertWeights, y_dtype=torch.float32):

@@ -83,7 +83,7 @@ def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torc
                  w1: torch.Tensor | None, out: torch.Tensor, *, K: int, N: int, row_index=None,
                  row_div: int = 1, s0=None, s1=None, group_size: int = 0, m_hint: int = 0, stream=None):
     """One grouped GEMM (see moe_grouped_gemm in include/moe.h).  Weights are dense
-    [n_groups][K][N] in the activation dtype, or int32 int4 words [n_groups][K/8][N] with bf16
+    [n_groups][N][K] in the activation dtype, or int32 int4 words [n_groups][K/8][N] with bf16
     scales s0/s1 [n_groups][K/group_size][N]."""
     _dev(a, group_offsets, w0, w1, out, row_index, s0, s1)
     args = _abi.MoeGemmArgs()

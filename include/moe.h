@@ -126,11 +126,14 @@ moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_loc
  * 4-bit weight scope: int4 weights stay packed in HBM and only the tiles in use are dequantised on
  * chip).  Group e covers output rows [group_offsets[e], group_offsets[e+1]); output row r uses
  * A row a[row_index[r] / row_div] (or a[r] when row_index is NULL) and expert e's weights.
- * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg[e][k][n]) * (sum_k A[k] Wu[e][k][n]).
- * DOWN:           out[r][n] = sum_k A[k] Wd[e][k][n].
+ * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg(e)[k][n]) * (sum_k A[k] Wu(e)[k][n]).
+ * DOWN:           out[r][n] = sum_k A[k] Wd(e)[k][n].
+ * W(e)[k][n] is stored as w[e][n][k] for dense weights (row n holds the K weights of output n,
+ * the [out][in] orientation of a linear layer) and as nibble k%8 of word [e][k/8][n] for int4.
  * bf16 path: bf16 operands, fp32 accumulation, bf16 or (DOWN) fp32 output; int4 weights are
  * dequantised to bf16 in LDS.  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are
- * not written.
+ * not written.  Limits (32-bit byte offsets): a_rows * K * sizeof(act) < 2^32 and
+ * K * N * sizeof(act) < 2^32, else MOE_ERR_UNSUPPORTED.
  */
 typedef struct moe_gemm_args {
   int32_t op;          /* moe_gemm_op */
@@ -150,7 +153,7 @@ typedef struct moe_gemm_args {
   const void* a;                 /* [a_rows][K] act dtype */
   const int32_t* row_index;      /* [rows_cap] (e.g. sorted_pairs) or NULL for identity rows */
   const int32_t* group_offsets;  /* [n_groups+1] non-decreasing, [0] = 0 (e.g. from moe_permute) */
-  const void* w0;      /* GATE_UP: Wg; DOWN: Wd.  Dense [n_groups][K][N]; int4 words [n_groups][K/8][N] */
+  const void* w0;      /* GATE_UP: Wg; DOWN: Wd.  Dense [n_groups][N][K]; int4 words [n_groups][K/8][N] */
   const void* w1;      /* GATE_UP: Wu (same layout as w0); DOWN: NULL */
   const void* s0;      /* int4: bf16 scales of w0 [n_groups][K/group_size][N]; dense: NULL */
   const void* s1;      /* int4: bf16 scales of w1; otherwise NULL */
