@@ -94,9 +94,10 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (a->n_groups < 1 || a->n_groups > 1024) return MOE_ERR_INVALID_ARG;
   if (a->rows_cap < 1 || a->a_rows < 1 || a->row_div < 1 || a->m_hint < 0) return MOE_ERR_INVALID_ARG;
   if (!a->row_index && a->a_rows < a->rows_cap) return MOE_ERR_INVALID_ARG;
-  // 32-bit byte offsets inside a and inside one expert's weight matrix
+  // 32-bit byte offsets inside a (below 2^31: offsets from 2^31 up mark rows that load nothing)
+  // and inside one expert's weight matrix
   const long long esz = a->act_dtype == MOE_DT_F32 ? 4 : 2;
-  if ((long long)a->a_rows * a->K * esz >= (1LL << 32) || (long long)a->K * a->N * esz >= (1LL << 32))
+  if ((long long)a->a_rows * a->K * esz >= (1LL << 31) || (long long)a->K * a->N * esz >= (1LL << 32))
     return MOE_ERR_UNSUPPORTED;
   if (a->wfmt == MOE_W_INT4_SYM_GROUP) {
     if (a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;

@@ -471,10 +471,12 @@ void k_gemm_bf16(GemmParams p) {
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int c = (tid + NT * i) % C::A_CHUNKS;
       const int r = c / (KC / 8), kc8 = c % (KC / 8);
-      const int rr = row0 + min(r, rows - 1);          // padding rows repeat the last valid row
+      const int rr = row0 + min(r, rows - 1);
       int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
-      t.a_off[i] = (uint32_t)(((size_t)src * p.K + kc8 * 8) * 2);
+      // Rows past the tile's last row load through an offset beyond the descriptor's range: the
+      // load returns zeros without a memory request (the host keeps a_rows * K * 2 below 2^31).
+      t.a_off[i] = r < rows ? (uint32_t)(((size_t)src * p.K + kc8 * 8) * 2) : 0x80000000u;
     }
     // piece i of a thread lands SLICE_ROWS * i rows below piece 0 (the swizzle repeats every 16 rows)
     t.a_lds = lds_off_rows((tid % C::A_CHUNKS) / (KC / 8), tid % (KC / 8));

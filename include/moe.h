@@ -132,7 +132,7 @@ moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_loc
  * the [out][in] orientation of a linear layer) and as nibble k%8 of word [e][k/8][n] for int4.
  * bf16 path: bf16 operands, fp32 accumulation, bf16 or (DOWN) fp32 output; int4 weights are
  * dequantised to bf16 in LDS.  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are
- * not written.  Limits (32-bit byte offsets): a_rows * K * sizeof(act) < 2^32 and
+ * not written.  Limits (32-bit byte offsets): a_rows * K * sizeof(act) < 2^31 and
  * K * N * sizeof(act) < 2^32, else MOE_ERR_UNSUPPORTED.
  */
 typedef struct moe_gemm_args {

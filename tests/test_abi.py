@@ -107,6 +107,9 @@ def _gemm(**kw):
     (dict(wfmt=1, group_size=128, s0=None, s1=FAKE), INV),
     (dict(wfmt=1, group_size=128, s0=FAKE, s1=None), INV),
     (dict(group_size=128), INV), (dict(s0=FAKE), INV),
+    # 32-bit offsets: activation bytes below 2^31, one expert matrix below 2^32
+    (dict(a_rows=1 << 17, K=8192), UNS), (dict(act_dtype=0, out_dtype=0, a_rows=1 << 17, K=4096), UNS),
+    (dict(K=65536, N=32768), UNS),
 ])
 def test_grouped_gemm_validation(L, kw, code):
     assert L.moe_grouped_gemm(ctypes.byref(_gemm(**kw)), None) == code
