@@ -52,12 +52,14 @@ def load(path: str = LIB_PATH):
     L.moe_status_string.argtypes, L.moe_status_string.restype = [i32], ctypes.c_char_p
     L.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.moe_pack_routing.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.moe_route_packed.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
     L.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
     L.moe_permute.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), vp]
     L.moe_combine.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp]
-    for fn in ("moe_route", "moe_pack_routing", "moe_permute", "moe_grouped_gemm", "moe_combine"):
+    for fn in ("moe_route", "moe_pack_routing", "moe_route_packed", "moe_permute", "moe_grouped_gemm",
+               "moe_combine"):
         getattr(L, fn).restype = i32
     _lib = L
     return L

@@ -50,7 +50,15 @@ MOE_API moe_status moe_route(const float* logits, int T, int E, int k, int32_t* 
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * E)) return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_w, as_stream(stream)));
+  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_w, nullptr, as_stream(stream)));
+}
+
+MOE_API moe_status moe_route_packed(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                                    int32_t* blob, void* stream) {
+  if (!logits || !blob || (topk_ids == nullptr) != (topk_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
+  if (!fits_i32((long long)T * E) || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_w, blob, as_stream(stream)));
 }
 
 MOE_API moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T, int k,
@@ -68,11 +76,12 @@ MOE_API size_t moe_permute_workspace_bytes(int T, int k, int e_local) {
 MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
                                int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (!blob || !sorted_pairs || !group_offsets || !pair_pos || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!blob || !sorted_pairs || !group_offsets || !pair_pos) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
   if (e_local < 1 || e_local > 1024 || e_first < 0 || !fits_i32((long long)e_first + e_local))
     return MOE_ERR_INVALID_ARG;
-  if (workspace_bytes < moe::permute_workspace_bytes(T, k, e_local)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::permute_workspace_bytes(T, k, e_local);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_permute(blob, T, k, e_first, e_local, sorted_pairs, group_offsets,
                                       pair_pos, workspace, as_stream(stream)));
 }

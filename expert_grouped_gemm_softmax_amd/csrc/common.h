@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
 }
 
 // Host-side launchers (one per source file); each returns hipSuccess or the launch error.
-hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* blob,
                         hipStream_t s);
 hipError_t launch_pack(const int32_t* ids, const float* w, int T, int k, int32_t* blob,
                        hipStream_t s);

@@ -4,8 +4,9 @@
 // (option B): each device keeps only the token-expert pairs routed to its own experts.  They are
 // grouped by expert with a stable counting sort: histogram, exclusive prefix scan, scatter.
 //
-// Two launches over chunks of kChunk consecutive pairs (one workgroup of 4 wavefronts per chunk,
-// 512 pairs per wavefront):
+// Up to kSmallPairs pairs: one launch, one workgroup of 16 wavefronts (k_perm_small): count per
+// wavefront in LDS, scan over experts, recount and write.  Larger inputs: two launches over chunks
+// of kChunk consecutive pairs (one workgroup of 4 wavefronts per chunk, 128 pairs per wavefront):
 //   k_perm_count    per-chunk histogram of local expert ids -> workspace counts[chunk][e];
 //   k_perm_scatter  every workgroup sums the counts of the chunks before it (its row base per
 //                   expert) and of all chunks (the group offsets), recounts its own chunk per
@@ -20,9 +21,11 @@ namespace moe {
 namespace {
 
 constexpr int kWavesPerChunk = 4;
-constexpr int kSteps = 8;                                  // 64-pair steps per wavefront
+constexpr int kSteps = 2;                                  // 64-pair steps per wavefront
 constexpr int kWavePairs = 64 * kSteps;
-constexpr int kChunk = kWavesPerChunk * kWavePairs;        // 2048 pairs per workgroup
+constexpr int kChunk = kWavesPerChunk * kWavePairs;        // 512 pairs per workgroup
+constexpr int kSmallWaves = 16;                            // single-workgroup path
+constexpr int kSmallPairs = 16384;
 
 __device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
   uint64_t same = __ballot(valid);
@@ -34,15 +37,17 @@ __device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
   return same;
 }
 
+// Local expert id of pair p (-1 outside [0, e_local) or p >= end).
+__device__ __forceinline__ int local_id(const int32_t* __restrict__ blob, int p, int end, int e_first, int e_local) {
+  const int id = (p < end) ? blob[min(p, end - 1)] : e_first - 1;
+  return (id >= e_first && id - e_first < e_local) ? id - e_first : -1;
+}
+
 // Local expert ids of this wavefront's pairs (-1 outside [0, e_local) or past the end).
 __device__ __forceinline__ void load_local_ids(const int32_t* __restrict__ blob, int beg, int end, int e_first,
                                                int e_local, int lane, int (&le)[kSteps]) {
 #pragma unroll
-  for (int u = 0; u < kSteps; ++u) {
-    const int p = beg + 64 * u + lane;
-    const int id = (p < end) ? blob[min(p, end - 1)] : e_first - 1;
-    le[u] = (id >= e_first && id - e_first < e_local) ? id - e_first : -1;
-  }
+  for (int u = 0; u < kSteps; ++u) le[u] = local_id(blob, beg + 64 * u + lane, end, e_first, e_local);
 }
 
 // Counts of this wavefront's pairs per local expert, accumulated into mine[0..e_local).
@@ -184,10 +189,83 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   }
 }
 
+// Whole permutation in one workgroup of kSmallWaves wavefronts; wavefront w owns the consecutive
+// pairs [w * span, (w + 1) * span), span a multiple of 64.  Pass 1 counts per wavefront, the
+// offsets and per-wavefront row bases come from one scan over the experts, pass 2 recounts in the
+// same order and writes the rows.
+__global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* __restrict__ blob, int P,
+                                                                 int e_first, int e_local, int nbits, int span,
+                                                                 int32_t* __restrict__ sorted_pairs,
+                                                                 int32_t* __restrict__ group_offsets,
+                                                                 int32_t* __restrict__ pair_pos) {
+  extern __shared__ int32_t lds[];                         // [kSmallWaves][e_local] counts -> row bases
+  int32_t* wsum = lds + kSmallWaves * e_local;             // [kSmallWaves]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int beg = wv * span, end = min(P, beg + span);
+  for (int i = threadIdx.x; i < kSmallWaves * e_local; i += blockDim.x) lds[i] = 0;
+  __syncthreads();
+  int32_t* mine = lds + wv * e_local;
+  for (int b = beg; b < end; b += 64) {
+    const int le = local_id(blob, b + lane, end, e_first, e_local);
+    const uint64_t same = match_local(le, le >= 0, nbits);
+    if (le >= 0 && lane == __ffsll((unsigned long long)same) - 1) mine[le] += __popcll(same);
+  }
+  __syncthreads();
+
+  // experts in blocks of blockDim.x: totals, exclusive scan, per-wavefront bases
+  int carry = 0;
+  for (int c0 = 0; c0 < e_local; c0 += blockDim.x) {
+    const int e = c0 + threadIdx.x;
+    int total = 0;
+    if (e < e_local)
+      for (int w = 0; w < kSmallWaves; ++w) total += lds[w * e_local + e];
+    int incl = total;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int wave_base = 0, block_total = 0;
+    for (int w = 0; w < kSmallWaves; ++w) {
+      wave_base += (w < wv) ? wsum[w] : 0;
+      block_total += wsum[w];
+    }
+    if (e < e_local) {
+      int run = carry + wave_base + incl - total;
+      group_offsets[e] = run;
+      for (int w = 0; w < kSmallWaves; ++w) {
+        const int c = lds[w * e_local + e];
+        lds[w * e_local + e] = run;
+        run += c;
+      }
+    }
+    carry += block_total;
+    __syncthreads();                                       // wsum reused by the next block
+  }
+  if (threadIdx.x == 0) group_offsets[e_local] = carry;
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b = beg; b < end; b += 64) {
+    const int p = b + lane;
+    const int le = local_id(blob, p, end, e_first, e_local);
+    const uint64_t same = match_local(le, le >= 0, nbits);
+    int row = -1;
+    if (le >= 0) row = mine[le] + __popcll(same & below);
+    if (le >= 0 && lane == __ffsll((unsigned long long)same) - 1) mine[le] += __popcll(same);
+    if (p < end) {
+      pair_pos[p] = row;
+      if (le >= 0) sorted_pairs[row] = p;
+    }
+  }
+}
+
 }  // namespace
 
 size_t permute_workspace_bytes(int T, int k, int e_local) {
   const long long P = (long long)T * k;
+  if (P <= kSmallPairs) return 0;
   const long long nchunks = (P + kChunk - 1) / kChunk;
   return (size_t)(nchunks * e_local * (long long)sizeof(int32_t));
 }
@@ -199,6 +277,13 @@ hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_
   const int nchunks = (P + kChunk - 1) / kChunk;
   int nbits = 1;
   while ((1 << nbits) < e_local) ++nbits;
+  if (P <= kSmallPairs) {
+    const int span = ((P + kSmallWaves - 1) / kSmallWaves + 63) / 64 * 64;
+    const size_t lds = sizeof(int32_t) * ((size_t)kSmallWaves * e_local + kSmallWaves);
+    k_perm_small<<<dim3(1), dim3(64 * kSmallWaves), lds, s>>>(blob, P, e_first, e_local, nbits, span,
+                                                              sorted_pairs, group_offsets, pair_pos);
+    return hipGetLastError();
+  }
   int32_t* counts = static_cast<int32_t*>(workspace);
   const size_t lds_count = sizeof(int32_t) * kWavesPerChunk * e_local;
   k_perm_count<<<dim3(nchunks), dim3(256), lds_count, s>>>(blob, P, e_first, e_local, nbits, counts);

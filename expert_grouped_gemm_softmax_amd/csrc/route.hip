@@ -61,9 +61,11 @@ __device__ __forceinline__ void dpp_step(float& bv, int& bid) {
   if (beats(ov, oid, bv, bid)) { bv = ov; bid = oid; }
 }
 
+// ids / w / blob: outputs (a NULL pointer is not written; ids and w are NULL together).
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
-                                               int32_t* __restrict__ ids, float* __restrict__ w) {
+                                               int32_t* __restrict__ ids, float* __restrict__ w,
+                                               int32_t* __restrict__ blob) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -120,8 +122,16 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 0));
   for (int j = 1; j < k; ++j) s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), j));
   if (lane < k) {
-    ids[(size_t)t * k + lane] = sel_id;
-    w[(size_t)t * k + lane] = e / s;                     // correctly rounded division
+    const float wt = e / s;                              // correctly rounded division
+    const size_t q = (size_t)t * k + lane;
+    if (ids) {
+      ids[q] = sel_id;
+      w[q] = wt;
+    }
+    if (blob) {                                          // the packed form: ids, then weight bits
+      blob[q] = sel_id;
+      blob[(size_t)T * k + q] = __float_as_int(wt);
+    }
   }
 }
 
@@ -136,14 +146,14 @@ __global__ __launch_bounds__(256) void k_pack(const int32_t* __restrict__ ids, c
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* blob,
                         hipStream_t s) {
   const dim3 grid((T + 3) / 4), block(256);
-  if (E <= 64) k_route<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else if (E <= 128) k_route<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else if (E <= 256) k_route<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else if (E <= 512) k_route<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else k_route<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  if (E <= 64) k_route<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, blob);
+  else if (E <= 128) k_route<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, blob);
+  else if (E <= 256) k_route<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, blob);
+  else if (E <= 512) k_route<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, blob);
+  else k_route<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, blob);
   return hipGetLastError();
 }
 

@@ -142,8 +142,7 @@ class MoELayer:
 
     # -- the steps, individually callable (the benchmark times them one by one) -----------------
     def step_route(self, logits, b, stream=None):
-        ops.route(logits, self.k, b.ids, b.w, stream=stream)
-        ops.pack_routing(b.ids, b.w, b.blob, stream=stream)
+        ops.route_packed(logits, self.k, b.ids, b.w, b.blob, stream=stream)
         ops.permute(b.blob, self.e_first, self.e_local, b.sorted_pairs, b.group_offsets, b.pair_pos,
                     workspace=b.workspace, stream=stream)
 

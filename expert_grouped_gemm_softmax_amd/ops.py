@@ -56,6 +56,25 @@ def pack_routing(ids: torch.Tensor, w: torch.Tensor, blob: torch.Tensor | None =
     return blob
 
 
+def route_packed(logits: torch.Tensor, k: int, ids: torch.Tensor | None = None, w: torch.Tensor | None = None,
+                 blob: torch.Tensor | None = None, write_ids: bool = True, stream=None):
+    """route + pack_routing in one launch -> (ids, w, blob); ids and w are None when write_ids is
+    False."""
+    T, E = logits.shape
+    assert logits.dtype == torch.float32
+    dev = logits.device
+    if write_ids:
+        ids = ids if ids is not None else torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = w if w is not None else torch.empty((T, k), dtype=torch.float32, device=dev)
+    else:
+        ids = w = None
+    blob = blob if blob is not None else torch.empty((2, T, k), dtype=torch.int32, device=dev)
+    _dev(logits, ids, w, blob)
+    check("moe_route_packed", load().moe_route_packed(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(blob),
+                                                      _stream(stream)))
+    return ids, w, blob
+
+
 def permute_workspace_bytes(T: int, k: int, e_local: int) -> int:
     return int(load().moe_permute_workspace_bytes(T, k, e_local))
 

@@ -97,6 +97,15 @@ moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T,
                             int32_t* blob, void* stream);
 
 /*
+ * moe_route_packed -- moe_route followed by moe_pack_routing in one launch: blob [2][T][k] as
+ * moe_pack_routing would build it from moe_route's outputs (bit for bit).  topk_ids and topk_w
+ * are written when both are non-NULL and skipped when both are NULL.
+ *   Limits: those of moe_route, and T * k < 2^31.
+ */
+moe_status moe_route_packed(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                            int32_t* blob, void* stream);
+
+/*
  * moe_permute -- keep the pairs routed to this device's experts and group them by expert
  * ("Systems engineering playbook ...", section 3, option B: each device filters and computes only
  * the inputs of its local experts).  Pair p = t*k + j is local iff
@@ -109,7 +118,8 @@ moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T,
  *   pair_pos      int32 [T*k]        out: row of pair p in sorted_pairs, or -1 if p is not local.
  *   workspace     device scratch of at least moe_permute_workspace_bytes(T, k, e_local) bytes
  *                 (per-chunk expert counts); its contents on entry do not matter.  Calls that
- *                 may run concurrently need separate workspaces.
+ *                 may run concurrently need separate workspaces.  When that size is 0 (T*k <=
+ *                 16384: one workgroup does the whole permutation) workspace may be NULL.
  *   Limits: 1 <= T, 1 <= k <= 64, 1 <= e_local <= 1024, e_first >= 0, T * k < 2^31.
  *   Deterministic: the output does not depend on scheduling.
  */

@@ -62,23 +62,37 @@ def test_route_validation(L):
     assert ok  # the valid form would launch; not called without a GPU
 
 
+def test_route_packed_validation(L):
+    bad = [
+        (None, 8, 16, 2, FAKE, FAKE, FAKE, None), (FAKE, 8, 16, 2, FAKE, FAKE, None, None),
+        (FAKE, 8, 16, 2, None, FAKE, FAKE, None), (FAKE, 8, 16, 2, FAKE, None, FAKE, None),
+        (FAKE, 0, 16, 2, FAKE, FAKE, FAKE, None), (FAKE, 8, 1025, 2, FAKE, FAKE, FAKE, None),
+        (FAKE, 8, 16, 0, None, None, FAKE, None), (FAKE, 8, 16, 17, None, None, FAKE, None),
+        (FAKE, 8, 512, 65, FAKE, FAKE, FAKE, None), (FAKE, 1 << 22, 1024, 2, None, None, FAKE, None),
+    ]
+    for args in bad:
+        assert L.moe_route_packed(*args) == INV, args
+
+
 def test_pack_and_permute_validation(L):
     assert L.moe_pack_routing(None, FAKE, 4, 2, FAKE, None) == INV
     assert L.moe_pack_routing(FAKE, FAKE, 4, 65, FAKE, None) == INV
     assert L.moe_pack_routing(FAKE, FAKE, 0, 2, FAKE, None) == INV
     assert L.moe_pack_routing(FAKE, FAKE, 1 << 26, 64, FAKE, None) == INV
-    ws = L.moe_permute_workspace_bytes(4, 2, 8)
-    assert ws == 8 * 4                                    # one chunk of per-expert counts
-    assert L.moe_permute_workspace_bytes(8192, 10, 64) == 40 * 64 * 4
+    assert L.moe_permute_workspace_bytes(4, 2, 8) == 0    # one workgroup: no workspace
+    assert L.moe_permute_workspace_bytes(2048, 8, 64) == 0  # 16384 pairs: still one workgroup
+    ws = L.moe_permute_workspace_bytes(2049, 8, 8)
+    assert ws == 33 * 8 * 4                               # 33 chunks of 512 pairs, per-expert counts
+    assert L.moe_permute_workspace_bytes(8192, 10, 64) == 160 * 64 * 4
     assert L.moe_permute_workspace_bytes(0, 2, 8) == 0
-    assert L.moe_permute(None, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, None, FAKE, FAKE, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 1025, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, -1, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 0, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, None, ws, None) == INV
-    assert L.moe_permute(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == INV
+    assert L.moe_permute(None, 2049, 8, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, None, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, 0, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, 0, 1025, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, -1, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 0, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, None, ws, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == INV
 
 
 def _gemm(**kw):

@@ -108,7 +108,8 @@ def test_routing_bit_exact_random_rank_zipf():
 @pytest.mark.parametrize("T,E,k,e_first,e_local", [
     (1, 4, 1, 0, 4), (3, 7, 7, 2, 5), (77, 64, 1, 0, 64), (129, 1024, 64, 0, 1024),
     (1000, 1024, 10, 512, 512), (257, 513, 33, 100, 413), (4096, 96, 6, 0, 1),
-    (65536, 512, 10, 64, 64), (5000, 128, 8, 120, 8), (64, 8, 2, 0, 8)])
+    (65536, 512, 10, 64, 64), (5000, 128, 8, 120, 8), (64, 8, 2, 0, 8),
+    (2048, 64, 8, 0, 64), (2049, 64, 8, 8, 40)])
 def test_routing_bit_exact_edge_shapes(T, E, k, e_first, e_local):
     rng = np.random.default_rng(T + E + k)
     L = (rng.standard_normal((T, E)) * 3).astype(np.float32)
@@ -118,6 +119,19 @@ def test_routing_bit_exact_edge_shapes(T, E, k, e_first, e_local):
         L[2, ::3] = 0.0
     cfg = W.MoEConfig("edge", T=T, H=64, E=E, k=k, I=64, e_first=e_first, e_local=e_local)
     _route_only(cfg, L)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (333, 96, 7), (4096, 512, 10), (1, 1024, 64)])
+def test_route_packed_equals_route_then_pack(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    L = torch.from_numpy((rng.standard_normal((T, E)) * 2).astype(np.float32)).to(_dev())
+    ids, w = ops.route(L, k)
+    blob = ops.pack_routing(ids, w)
+    ids2, w2, blob2 = ops.route_packed(L, k)
+    _, _, blob3 = ops.route_packed(L, k, write_ids=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(blob, blob2) and torch.equal(blob, blob3)
 
 
 def test_permute_with_no_local_pair():
