@@ -25,7 +25,8 @@ constexpr int kSteps = 2;                                  // 64-pair steps per 
 constexpr int kWavePairs = 64 * kSteps;
 constexpr int kChunk = kWavesPerChunk * kWavePairs;        // 512 pairs per workgroup
 constexpr int kSmallWaves = 16;                            // single-workgroup path
-constexpr int kSmallPairs = 16384;
+constexpr int kSmallSteps = 16;                            // 64-pair steps per wavefront at most
+constexpr int kSmallPairs = kSmallWaves * kSmallSteps * 64;   // 16384
 
 __device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
   uint64_t same = __ballot(valid);
@@ -93,6 +94,9 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   int32_t* base = lds + kWavesPerChunk * e_local;          // [e_local] chunk base per expert
   int32_t* wsum = base + e_local;                          // [4]
   int32_t* allc = wsum + kWavesPerChunk;                   // [nchunks][e_local] when ALL_IN_LDS
+  int32_t* pbef = allc + (size_t)nchunks * e_local;        // [parts][e_local] when ALL_IN_LDS
+  const int parts = ALL_IN_LDS ? max(1, (int)blockDim.x / e_local) : 1;
+  int32_t* ptot = pbef + parts * e_local;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int chunk = blockIdx.x;
   const int beg = chunk * kChunk + wv * kWavePairs;
@@ -107,6 +111,21 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
   count_wave(le, nbits, lane, cnt + wv * e_local);
+  if constexpr (ALL_IN_LDS) {
+    // thread (part, e) sums chunks [part, part+1) * nchunks / parts of expert e
+    for (int i = threadIdx.x; i < parts * e_local; i += blockDim.x) {
+      const int part = i / e_local, e = i % e_local;
+      int bsum = 0, tsum = 0;
+      for (int c = part * nchunks / parts; c < (part + 1) * nchunks / parts; ++c) {
+        const int v = allc[c * e_local + e];
+        bsum += (c < chunk) ? v : 0;
+        tsum += v;
+      }
+      pbef[i] = bsum;
+      ptot[i] = tsum;
+    }
+    __syncthreads();
+  }
 
   // Per expert: pairs in earlier chunks and in all chunks; then the offsets (scan over experts).
   int carry = 0;
@@ -115,10 +134,9 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
     int before = 0, total = 0;
     if (e < e_local) {
       if constexpr (ALL_IN_LDS) {
-        for (int c = 0; c < nchunks; ++c) {
-          const int v = allc[c * e_local + e];
-          before += (c < chunk) ? v : 0;
-          total += v;
+        for (int part = 0; part < parts; ++part) {
+          before += pbef[part * e_local + e];
+          total += ptot[part * e_local + e];
         }
       } else {
         int c = 0;
@@ -202,13 +220,18 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* 
   int32_t* wsum = lds + kSmallWaves * e_local;             // [kSmallWaves]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int beg = wv * span, end = min(P, beg + span);
+  // all of this wavefront's ids in registers, loaded at once (span <= 64 * kSmallSteps)
+  int le[kSmallSteps];
+#pragma unroll
+  for (int u = 0; u < kSmallSteps; ++u) le[u] = local_id(blob, beg + 64 * u + lane, end, e_first, e_local);
   for (int i = threadIdx.x; i < kSmallWaves * e_local; i += blockDim.x) lds[i] = 0;
   __syncthreads();
   int32_t* mine = lds + wv * e_local;
-  for (int b = beg; b < end; b += 64) {
-    const int le = local_id(blob, b + lane, end, e_first, e_local);
-    const uint64_t same = match_local(le, le >= 0, nbits);
-    if (le >= 0 && lane == __ffsll((unsigned long long)same) - 1) mine[le] += __popcll(same);
+#pragma unroll
+  for (int u = 0; u < kSmallSteps; ++u) {
+    if (beg + 64 * u >= end) break;                        // wavefront-uniform
+    const uint64_t same = match_local(le[u], le[u] >= 0, nbits);
+    if (le[u] >= 0 && lane == __ffsll((unsigned long long)same) - 1) mine[le[u]] += __popcll(same);
   }
   __syncthreads();
 
@@ -247,16 +270,17 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* 
   if (threadIdx.x == 0) group_offsets[e_local] = carry;
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b = beg; b < end; b += 64) {
-    const int p = b + lane;
-    const int le = local_id(blob, p, end, e_first, e_local);
-    const uint64_t same = match_local(le, le >= 0, nbits);
+#pragma unroll
+  for (int u = 0; u < kSmallSteps; ++u) {
+    if (beg + 64 * u >= end) break;                        // wavefront-uniform
+    const int p = beg + 64 * u + lane;
+    const uint64_t same = match_local(le[u], le[u] >= 0, nbits);
     int row = -1;
-    if (le >= 0) row = mine[le] + __popcll(same & below);
-    if (le >= 0 && lane == __ffsll((unsigned long long)same) - 1) mine[le] += __popcll(same);
+    if (le[u] >= 0) row = mine[le[u]] + __popcll(same & below);
+    if (le[u] >= 0 && lane == __ffsll((unsigned long long)same) - 1) mine[le[u]] += __popcll(same);
     if (p < end) {
       pair_pos[p] = row;
-      if (le >= 0) sorted_pairs[row] = p;
+      if (le[u] >= 0) sorted_pairs[row] = p;
     }
   }
 }
@@ -290,7 +314,7 @@ hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t lds_scatter = sizeof(int32_t) * ((kWavesPerChunk + 1) * e_local + kWavesPerChunk);
-  const size_t lds_all = sizeof(int32_t) * (size_t)nchunks * e_local;
+  const size_t lds_all = sizeof(int32_t) * ((size_t)nchunks * e_local + 2 * (size_t)max(256, e_local));
   if (lds_scatter + lds_all <= 96 * 1024)
     k_perm_scatter<true><<<dim3(nchunks), dim3(256), lds_scatter + lds_all, s>>>(
         blob, P, e_first, e_local, nbits, nchunks, counts, sorted_pairs, group_offsets, pair_pos);

@@ -5,10 +5,10 @@
 // renormalised weight sequence stated in moe.h.  The blob layout follows section 3 (3-to-2
 // all-gather: ids and weight bits stacked on a new leading axis in one int32 array).
 //
-// One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers,
-// sorted once per lane; each of the k rounds is a 4-step DPP reduction of the lane heads inside
-// each 16-lane row and a comparison of the four row winners read with v_readlane (key: larger
-// logit, then smaller expert id).  The weights need no E-term reduction: slot j's
+// One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers as
+// 64-bit selection keys (logit order, then lower expert id), sorted once per lane; each of the k
+// rounds is a 4-step DPP max of the lane heads inside each 16-lane row and a max of the four row
+// winners read with v_readlane.  The weights need no E-term reduction: slot j's
 // weight only involves the k selected logits.
 #include "common.h"
 
@@ -42,23 +42,36 @@ __device__ __forceinline__ float exp_neg(float d) {
   return p * two_n;                                        // exact: the product stays normal
 }
 
-constexpr int kNone = 0x7fffffff;
-
-// (v, id) beats (bv, bid): larger logit, or equal logit (-0 == +0) and smaller id.
-__device__ __forceinline__ bool beats(float v, int id, float bv, int bid) {
-  if (id == kNone) return false;
-  if (bid == kNone) return true;
-  return v > bv || (v == bv && id < bid);
+// Selection key of (logit v, expert id): larger key = selected first.  High word: the fp32 bits of
+// v mapped to an unsigned order (-0 folded onto +0); low word: ~id, so equal logits go to the lower
+// id.  Key 0 marks an empty slot (every finite logit maps above it).
+__device__ __forceinline__ uint64_t route_key(float v, int id) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;                            // -0 equals +0
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)~id;
 }
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t b = (uint32_t)(key >> 32);
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
 
 // DPP controls (gfx9 encoding): quad permutations, reverse within 8 lanes, reverse within 16.
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 
 template <int CTRL>
-__device__ __forceinline__ void dpp_step(float& bv, int& bid) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xf, 0xf, false));
-  const int oid = __builtin_amdgcn_update_dpp(0, bid, CTRL, 0xf, 0xf, false);
-  if (beats(ov, oid, bv, bid)) { bv = ov; bid = oid; }
+__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t k, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ids / w / blob: outputs (a NULL pointer is not written; ids and w are NULL together).
@@ -71,52 +84,46 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                     // uniform per wave
   const float* row = logits + (size_t)t * E;
-  // Lane l owns experts l, l+64, ...; its list is sorted once by the selection key, so each round
-  // only compares the heads of the 64 lists and the winning lane drops its head.
-  float v[PER_LANE];
-  int id[PER_LANE];
+  // Lane l owns experts l, l+64, ...; its keys are sorted once (descending), so each round only
+  // compares the heads of the 64 lists and the winning lane drops its head.
+  uint64_t key[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
-    v[i] = 0.0f;
-    id[i] = kNone;
-    if (e < E) { v[i] = __builtin_nontemporal_load(row + e); id[i] = e; }
+    key[i] = (e < E) ? route_key(__builtin_nontemporal_load(row + e), e) : 0ull;
   }
 #pragma unroll
   for (int i = 1; i < PER_LANE; ++i)                      // insertion sort, fully unrolled
 #pragma unroll
-    for (int j = i; j > 0; --j)
-      if (beats(v[j], id[j], v[j - 1], id[j - 1])) {
-        const float tv = v[j]; v[j] = v[j - 1]; v[j - 1] = tv;
-        const int ti = id[j]; id[j] = id[j - 1]; id[j - 1] = ti;
-      }
-  float sel_v = 0.0f;   // slot `lane` (lanes < k)
-  int sel_id = 0;
+    for (int j = i; j > 0; --j) {
+      const uint64_t a = key[j - 1], b2 = key[j];
+      key[j - 1] = a > b2 ? a : b2;
+      key[j] = a > b2 ? b2 : a;
+    }
+  uint64_t sel = 0;                                       // slot `lane` (lanes < k)
   for (int j = 0; j < k; ++j) {
-    float bv = v[0];
-    int bid = id[0];
-    // best head of each 16-lane row, in every lane of that row
-    dpp_step<kQuadXor1>(bv, bid);
-    dpp_step<kQuadXor2>(bv, bid);
-    dpp_step<kRowHalfMirror>(bv, bid);
-    dpp_step<kRowMirror>(bv, bid);
-    // best of the four rows (read as wave-uniform values)
-    float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-    int wid = __builtin_amdgcn_readlane(bid, 0);
+    uint64_t m = key[0];
+    // largest head of each 16-lane row, in every lane of that row
+    m = dpp_max<kQuadXor1>(m);
+    m = dpp_max<kQuadXor2>(m);
+    m = dpp_max<kRowHalfMirror>(m);
+    m = dpp_max<kRowMirror>(m);
+    // largest of the four rows (wave-uniform)
+    uint64_t best = readlane64(m, 0);
 #pragma unroll
     for (int r = 16; r < 64; r += 16) {
-      const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r));
-      const int rid = __builtin_amdgcn_readlane(bid, r);
-      if (beats(rv, rid, wv, wid)) { wv = rv; wid = rid; }
+      const uint64_t o = readlane64(m, r);
+      best = o > best ? o : best;
     }
-    if (lane == (wid & 63)) {                             // the winner's list advances
+    if (key[0] == best) {                                 // the winner's list advances
 #pragma unroll
-      for (int i = 0; i + 1 < PER_LANE; ++i) { v[i] = v[i + 1]; id[i] = id[i + 1]; }
-      v[PER_LANE - 1] = 0.0f;
-      id[PER_LANE - 1] = kNone;
+      for (int i = 0; i + 1 < PER_LANE; ++i) key[i] = key[i + 1];
+      key[PER_LANE - 1] = 0ull;
     }
-    if (lane == j) { sel_v = wv; sel_id = wid; }
+    if (lane == j) sel = best;
   }
+  const float sel_v = key_value(sel);
+  const int sel_id = key_id(sel);
   const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
   const float e = (lane < k) ? exp_neg(sel_v - m) : 0.0f;
   float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 0));
