@@ -81,7 +81,8 @@ MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, i
   if (e_local < 1 || e_local > 1024 || e_first < 0 || !fits_i32((long long)e_first + e_local))
     return MOE_ERR_INVALID_ARG;
   const size_t need = moe::permute_workspace_bytes(T, k, e_local);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0))
+    return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_permute(blob, T, k, e_first, e_local, sorted_pairs, group_offsets,
                                       pair_pos, workspace, as_stream(stream)));
 }

@@ -53,17 +53,22 @@ __global__ __launch_bounds__(256) void k_combine(const TA* __restrict__ o, const
   __shared__ int s_n;
   const int t = blockIdx.x;
   const int64_t P = (int64_t)T * k;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int j = 0; j < k; ++j) {
-      const int pos = pair_pos[(int64_t)t * k + j];
-      if (pos >= 0 && pos < rows) {
-        s_pos[n] = pos;
-        s_w[n] = __int_as_float(blob[P + (int64_t)t * k + j]);
-        ++n;
-      }
+  if (threadIdx.x < 64) {                                // wave 0 compacts the token's valid slots in order
+    const int j = threadIdx.x;
+    int pos = -1;
+    float wj = 0.f;
+    if (j < k) {
+      pos = pair_pos[(int64_t)t * k + j];
+      wj = __int_as_float(blob[P + (int64_t)t * k + j]);
     }
-    s_n = n;
+    const bool valid = j < k && pos >= 0 && pos < rows;
+    const uint64_t m = __ballot(valid);
+    if (valid) {
+      const int slot = __popcll(m & ((1ull << j) - 1ull));
+      s_pos[slot] = pos;
+      s_w[slot] = wj;
+    }
+    if (j == 0) s_n = __popcll(m);
   }
   __syncthreads();
   const int n = s_n;

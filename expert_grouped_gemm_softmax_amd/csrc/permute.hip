@@ -106,7 +106,26 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   int le[kSteps];
   load_local_ids(blob, beg, end, e_first, e_local, lane, le);
   if constexpr (ALL_IN_LDS) {
-    for (int i = threadIdx.x; i < nchunks * e_local; i += blockDim.x) allc[i] = counts[i];
+    // 16-byte loads, eight in flight per thread (the host checks the workspace is 16-byte
+    // aligned; a tail of fewer than four counts is copied one by one)
+    const int n = nchunks * e_local, n4 = n / 4;
+    const int4* c4 = reinterpret_cast<const int4*>(counts);
+    for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * blockDim.x) {
+      int4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * blockDim.x;
+        v[u] = c4[min(i, n4 - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * blockDim.x;
+        if (i < n4) {
+          allc[4 * i] = v[u].x; allc[4 * i + 1] = v[u].y; allc[4 * i + 2] = v[u].z; allc[4 * i + 3] = v[u].w;
+        }
+      }
+    }
+    for (int i = 4 * n4 + threadIdx.x; i < n; i += blockDim.x) allc[i] = counts[i];
   }
   for (int i = threadIdx.x; i < kWavesPerChunk * e_local; i += blockDim.x) cnt[i] = 0;
   __syncthreads();

@@ -116,8 +116,8 @@ moe_status moe_route_packed(const float* logits, int T, int E, int k, int32_t* t
  *   group_offsets int32 [e_local+1]  out: group e owns rows [off[e], off[e+1]); off[0] = 0,
  *                                    off[e_local] = n_loc.
  *   pair_pos      int32 [T*k]        out: row of pair p in sorted_pairs, or -1 if p is not local.
- *   workspace     device scratch of at least moe_permute_workspace_bytes(T, k, e_local) bytes
- *                 (per-chunk expert counts); its contents on entry do not matter.  Calls that
+ *   workspace     device scratch of at least moe_permute_workspace_bytes(T, k, e_local) bytes,
+ *                 16-byte aligned (per-chunk expert counts); its contents on entry do not matter.  Calls that
  *                 may run concurrently need separate workspaces.  When that size is 0 (T*k <=
  *                 16384: one workgroup does the whole permutation) workspace may be NULL.
  *   Limits: 1 <= T, 1 <= k <= 64, 1 <= e_local <= 1024, e_first >= 0, T * k < 2^31.

@@ -93,6 +93,7 @@ def test_pack_and_permute_validation(L):
     assert L.moe_permute(FAKE, 2049, 0, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == INV
     assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, None, ws, None) == INV
     assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == INV
+    assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, FAKE + 4, ws, None) == INV   # alignment
 
 
 def _gemm(**kw):
