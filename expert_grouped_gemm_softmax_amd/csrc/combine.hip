@@ -44,7 +44,7 @@ template <> struct Vec8<float> {
 };
 
 template <typename TA, typename TY>
-__global__ __launch_bounds__(256) void k_combine(const TA* __restrict__ o, const int32_t* __restrict__ blob,
+__global__ __launch_bounds__(512) void k_combine(const TA* __restrict__ o, const int32_t* __restrict__ blob,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const TA* __restrict__ shared, int T, int k, int H,
                                                  int rows, TY* __restrict__ y) {
@@ -74,12 +74,19 @@ __global__ __launch_bounds__(256) void k_combine(const TA* __restrict__ o, const
   const int n = s_n;
   for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < n; ++j) {
-      float v[8];
-      Vec8<TA>::load(o + (size_t)s_pos[j] * H + h, v);
-      const float wj = s_w[j];
+    // rows in batches of four: the loads of a batch are in flight together, the sum keeps slot order
+    for (int j0 = 0; j0 < n; j0 += 4) {
+      float v[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n) Vec8<TA>::load(o + (size_t)s_pos[j0 + u] * H + h, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n) {
+          const float wj = s_w[j0 + u];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[u][i], acc[i]);
+        }
     }
     if (shared) {
       float v[8];
@@ -95,7 +102,7 @@ template <typename TA, typename TY>
 hipError_t run(const void* o, const int32_t* blob, const int32_t* pair_pos, const void* shared, int T,
                int k, int H, int rows, void* y, hipStream_t s) {
   int threads = H / 8;
-  if (threads > 256) threads = 256;
+  if (threads > 512) threads = 512;
   threads = ((threads + 63) / 64) * 64;
   k_combine<TA, TY><<<dim3(T), dim3(threads), 0, s>>>(static_cast<const TA*>(o), blob, pair_pos,
                                                       static_cast<const TA*>(shared), T, k, H, rows,
