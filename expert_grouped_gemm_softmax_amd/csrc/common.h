@@ -27,14 +27,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ u16 f32_to_bf16(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
 
-// v_perm_b32 byte selects: {lo halves of x and y}, {hi halves of x and y} -> x in bits 0..15.
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);
-}
-
 // Host-side launchers (one per source file); each returns hipSuccess or the launch error.
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* blob,
                         hipStream_t s);

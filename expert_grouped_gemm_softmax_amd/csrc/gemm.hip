@@ -635,20 +635,20 @@ constexpr bool cfg_ok() {
 }
 
 template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
-hipError_t run_gu(const GemmParams& p, bool q4, int wgs, hipStream_t s) {
+hipError_t run_gu(const GemmParams& p, bool q4, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, true>(), "gate/up tile");
-  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>, u16>(p, wgs ? wgs : WGS, s)
-            : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS, RS>, u16>(p, wgs ? wgs : WGS, s);
+  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>, u16>(p, WGS, s)
+            : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS, RS>, u16>(p, WGS, s);
 }
 
 template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
-hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, int wgs, hipStream_t s) {
+hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, false>(), "down tile");
   if (f32out)
-    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, float>(p, wgs ? wgs : WGS, s)
-              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, float>(p, wgs ? wgs : WGS, s);
-  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, u16>(p, wgs ? wgs : WGS, s)
-            : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, u16>(p, wgs ? wgs : WGS, s);
+    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, float>(p, WGS, s)
+              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, float>(p, WGS, s);
+  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, u16>(p, WGS, s)
+            : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, u16>(p, WGS, s);
 }
 
 int env_int(const char* name, int dflt) {
@@ -658,8 +658,7 @@ int env_int(const char* name, int dflt) {
 
 }  // namespace
 
-static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, int wgs,
-                                 hipStream_t s);
+static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, hipStream_t s);
 
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   GemmParams p;
@@ -672,51 +671,31 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  int v = small_m ? 0 : 7;
+  int v = small_m ? 0 : 1;
   v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
-  hipError_t err = launch_variant(p, v, gu, q4, f32out, env_int(gu ? "MOE_GEMM_WGS_GU" : "MOE_GEMM_WGS_DN", 0), s);
-  if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrowest tiles
-    err = launch_variant(p, small_m ? 0 : 8, gu, q4, f32out, 0, s);
+  hipError_t err = launch_variant(p, v, gu, q4, f32out, s);
+  if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrower tiles
+    err = launch_variant(p, small_m ? 0 : 2, gu, q4, f32out, s);
   return err;
 }
 
-static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, int wgs,
-                                 hipStream_t s) {
-  // Variant ids: rows x columns per tile for gate/up | down, waves per workgroup, LDS buffers,
-  // workgroups per CU.
-  //   0: 32x64 | 32x128,   4 waves, 1 buffer, 4/CU     1: 32x128 | 32x256, 8 waves, 1 buffer, 2/CU
-  //   2: 128x64 | 128x128, 4 waves, 2 buffers, 2/CU    3: 128x128 | 128x256, 8 waves, 2 buffers, 1/CU
-  //   4: 64x64 | 64x128,   4 waves, 2 buffers, 3/CU    5: 32x128 | 32x256, 4 waves, 1 buffer, 2/CU
-  //   6: 128x128 | 128x256, 8 waves (4x2), 2 buffers, 1/CU
-  //   7: 256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU, one chunk in registers
-  //   8: 256x64 | 256x128, 4 waves (4x1), 2 buffers, 1/CU
-  //   9: 256x128 | 256x256, 4 waves (4x1), 2 buffers, 1/CU
+static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, hipStream_t s) {
+  // Tile shapes: rows x columns per tile for gate/up | down, waves, LDS buffers, workgroups per CU.
+  //   0 (decode):          32x64   | 32x128,  4 waves (1x4), 1 buffer,  4/CU, two chunks in registers
+  //   1 (prefill):         256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU, one chunk in registers
+  //   2 (prefill, narrow): 256x64  | 256x128, 4 waves (4x1), 2 buffers, 1/CU, two chunks in registers
   const bool n256 = p.N % 256 == 0;
   if (gu) {
     switch (v) {
-      case 0: return run_gu<32, 64, 1, 4, 1, 4>(p, q4, wgs, s);
-      case 1: return run_gu<32, 128, 1, 8, 1, 2>(p, q4, wgs, s);
-      case 3: return run_gu<128, 128, 2, 4, 2, 1>(p, q4, wgs, s);
-      case 4: return run_gu<64, 64, 2, 2, 2, 3>(p, q4, wgs, s);
-      case 5: return run_gu<32, 128, 1, 4, 1, 2>(p, q4, wgs, s);
-      case 6: return run_gu<128, 128, 4, 2, 2, 1>(p, q4, wgs, s);
-      case 7: return run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, wgs, s);
-      case 8: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, wgs, s);
-      case 9: return run_gu<256, 128, 4, 1, 2, 1>(p, q4, wgs, s);
-      default: return run_gu<128, 64, 2, 2, 2, 2>(p, q4, wgs, s);
+      case 0: return run_gu<32, 64, 1, 4, 1, 4>(p, q4, s);
+      case 1: return run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, s);
+      default: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, s);
     }
   }
   switch (v) {
-    case 0: return run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, wgs, s);
-    case 1: return n256 ? run_dn<32, 256, 1, 8, 1, 2>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    case 3: return n256 ? run_dn<128, 256, 2, 4, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    case 4: return run_dn<64, 128, 2, 2, 2, 3>(p, q4, f32out, wgs, s);
-    case 5: return n256 ? run_dn<32, 256, 1, 4, 1, 2>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    case 6: return n256 ? run_dn<128, 256, 4, 2, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    case 7: return n256 ? run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    case 8: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, wgs, s);
-    case 9: return n256 ? run_dn<256, 256, 4, 1, 2, 1>(p, q4, f32out, wgs, s) : hipErrorInvalidValue;
-    default: return run_dn<128, 128, 2, 2, 2, 2>(p, q4, f32out, wgs, s);
+    case 0: return run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, s);
+    case 1: return n256 ? run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s) : hipErrorInvalidValue;
+    default: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, s);
   }
 }
 
