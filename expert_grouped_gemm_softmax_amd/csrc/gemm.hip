@@ -89,6 +89,27 @@ struct TileIter {
   int next, end, step;
 };
 
+struct TileCoord {
+  int e, row0, rows, n0;
+};
+
+// Tile -> (expert, first output row, rows, first column).  Inside an expert, tiles go in groups
+// of up to 4 m-tiles x all n-tiles, m-tile fastest: the workgroups of one XCD then share a few
+// activation tiles and a few weight slabs in L2.
+__device__ __forceinline__ TileCoord tile_coord(const int* s_tstart, const int* s_goff, int n_groups, int tile,
+                                                int BM, int BN, int tiles_n) {
+  constexpr int kGroupM = 4;
+  const int e = find_group(s_tstart, n_groups, tile);
+  const int g0 = s_goff[e], g1 = s_goff[e + 1];
+  const int mtiles = (g1 - g0 + BM - 1) / BM;
+  const int local = tile - s_tstart[e];
+  const int grp = local / (kGroupM * tiles_n), in_grp = local % (kGroupM * tiles_n);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int mt = grp * kGroupM + in_grp % gm, nt = in_grp / gm;
+  const int row0 = g0 + mt * BM;
+  return {e, row0, min(BM, g1 - row0), nt * BN};
+}
+
 // XCD-aware static schedule over [0, total).
 __device__ __forceinline__ TileIter tile_range(int total) {
   const int G = gridDim.x;               // a multiple of 8
@@ -448,19 +469,8 @@ void k_gemm_bf16(GemmParams p) {
   const uint32_t s_bytes = C::Q4 ? (uint32_t)((size_t)(p.K / p.group_size) * p.N * 2) : 0u;
 
   for (int tile = it.next; tile < it.end; tile += it.step) {
-    const int e = find_group(s_tstart, p.n_groups, tile);
-    const int g0 = s_goff[e], g1 = s_goff[e + 1];
-    const int mtiles = (g1 - g0 + BM - 1) / BM;
-    const int local = tile - s_tstart[e];
-    // Inside an expert, tiles go in groups of up to kGroupM m-tiles x all n-tiles, m-tile fastest:
-    // the workgroups of one XCD then share a few activation tiles and a few weight slabs in L2.
-    constexpr int kGroupM = 4;
-    const int grp = local / (kGroupM * tiles_n), in_grp = local % (kGroupM * tiles_n);
-    const int gm = min(kGroupM, mtiles - grp * kGroupM);
-    const int mt = grp * kGroupM + in_grp % gm, nt = in_grp / gm;
-    const int row0 = g0 + mt * BM;
-    const int rows = min(BM, g1 - row0);
-    const int n0 = nt * BN;
+    const TileCoord tc = tile_coord(s_tstart, s_goff, p.n_groups, tile, BM, BN, tiles_n);
+    const int e = tc.e, row0 = tc.row0, rows = tc.rows, n0 = tc.n0;
     const int nm = min(C::MT, max(0, ((rows + 15) / 16 - wm + WM - 1) / WM));   // live 16-row tiles
 
     TileCtx<C> t;
@@ -516,6 +526,207 @@ void k_gemm_bf16(GemmParams p) {
     }
     tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0);
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 MFMA kernel with direct global -> LDS loads (dense weights, prefill tiles)
+// ---------------------------------------------------------------------------------------------
+// Same tiles, LDS layout, operand reads and epilogue as k_gemm_bf16, but activation rows and
+// weight rows go from global memory straight into LDS (buffer_load_dwordx4 ... lds): no staging
+// registers, no ds_write instructions, so more of the issue slots and registers stay with the
+// MFMA stream.  One load instruction fills 8 consecutive 128-byte rows (lane i writes the 16 bytes
+// at M0 + 16 i), so the row swizzle is applied on the global side: lane i loads the chunk that
+// belongs at position i % 8 of row i / 8.  Two LDS buffers: while chunk kc is multiplied from one,
+// chunk kc + 1 streams into the other.
+//
+// The loads are issued from inline assembly, which the compiler's wait-count tracking does not
+// see (with the compiler's own LDS-load intrinsic it waits for every outstanding load before each
+// LDS read, which serialises the pipeline): the kernel waits for them itself (s_waitcnt vmcnt(0)
+// before the barrier that publishes a buffer; vector memory operations of a wave complete in
+// issue order, and any other outstanding vector memory operation only makes the wait longer).
+template <int BM_, int BN_, int WM_, int WN_, bool GU_>
+struct DCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool GU = GU_;
+  static constexpr int NWAVES = WM * WN, NT = 64 * NWAVES;
+  static constexpr int WAVES_PER_SIMD = (NWAVES + 3) / 4;
+  static constexpr int KC = 64, NW = GU ? 2 : 1;
+  static constexpr int A_ELEMS = BM * 64, B_ELEMS = NW * BN * 64, STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int A_INST = BM / 8 / NWAVES, B_INST = NW * BN / 8 / NWAVES;
+  static constexpr int MT = BM / WM / 16, NTL = BN / WN / 16;
+  static_assert(A_INST >= 1 && B_INST >= 1 && BM % (8 * NWAVES) == 0 && BN % 8 == 0, "row blocks");
+  static_assert(NWAVES % 2 == 0, "8-row block parity equals the wave's parity (global-side swizzle)");
+  static size_t lds_bytes(int n_groups) { return 2 * (size_t)STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
+};
+
+// One 16-byte-per-lane load into LDS: lane i's data lands at lds + 16 i (lds wave-uniform).  M0 is
+// not used by anything else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"      // m0 is a reserved register; listing it is deliberate
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <class C>
+struct DmaCtx {
+  __amdgpu_buffer_rsrc_t ar, wr[C::NW];             // activation matrix; the tile's expert weights
+  uint32_t a_voff[C::A_INST];                       // lane's activation row piece per block (rows past the tile: out of range)
+  uint32_t b_voff;                                  // lane's offset inside an 8-row weight block
+  uint32_t b_soff[C::B_INST];                       // wave-uniform offset of each weight block
+  int b_m[C::B_INST];                               // matrix of each weight block
+  uint32_t lds;                                     // LDS address of buffer 0
+  int wave, nK;
+};
+
+template <class C>
+__device__ __forceinline__ void dma_chunk(const DmaCtx<C>& t, int kc, int stage) {
+  const uint32_t st = t.lds + (uint32_t)stage * C::STAGE * 2;
+  const uint32_t koff = (uint32_t)kc * 128;
+#pragma unroll
+  for (int j = 0; j < C::A_INST; ++j) lds_dma16(t.ar, t.a_voff[j], koff, st + 8 * (t.wave + C::NWAVES * j) * 128);
+#pragma unroll
+  for (int j = 0; j < C::B_INST; ++j) {
+    __amdgpu_buffer_rsrc_t w = t.wr[0];
+    if constexpr (C::NW == 2) w = t.b_m[j] ? t.wr[1] : t.wr[0];
+    lds_dma16(w, t.b_voff, t.b_soff[j] + koff, st + C::A_ELEMS * 2 + 8 * (t.wave + C::NWAVES * j) * 128);
+  }
+}
+
+template <class C, typename OutT, int NM>
+__device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O, int N, int lane, int wrow0, int wcol0,
+                                         const TileCoord& tc) {
+  f32x4 acc[C::NW][NM > 0 ? NM : 1][C::NTL];
+#pragma unroll
+  for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+    for (int i = 0; i < (NM > 0 ? NM : 1); ++i)
+#pragma unroll
+      for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int arow = wrow0 + (lane & 15), bcol = wcol0 + (lane & 15), kofs = (lane >> 4) * 8;
+  const int nK = t.nK;
+  wait_vmcnt0();
+  dma_chunk(t, 0, 0);
+  for (int kc = 0; kc < nK; ++kc) {
+    wait_vmcnt0();                                 // this wave's loads of chunk kc
+    __syncthreads();                               // everyone's; and the other buffer is free
+    if (kc + 1 < nK) dma_chunk(t, kc + 1, (kc + 1) & 1);
+    if constexpr (NM > 0) {
+      const u16* sA = smem + (kc & 1) * C::STAGE;
+      const u16* sB = sA + C::A_ELEMS;
+#pragma unroll
+      for (int ks = 0; ks < C::KC; ks += 32) {
+        bf16x8 av[NM];
+#pragma unroll
+        for (int i = 0; i < NM; ++i)
+          av[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off_rows(arow, (ks + kofs) >> 3) + i * 16 * C::WM * 64);
+#pragma unroll
+        for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+          for (int j = 0; j < C::NTL; ++j) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64);
+#pragma unroll
+            for (int i = 0; i < NM; ++i)
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
+          }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wrow0 + i * 16 * C::WM + (lane >> 4) * 4 + r;
+        const int col = wcol0 + j * 16 + (lane & 15);
+        if (row < tc.rows) {
+          float v;
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
+          else v = acc[0][i][j][r];
+          OutT* dst = O + (size_t)(tc.row0 + row) * N + tc.n0 + col;
+          if constexpr (sizeof(OutT) == 4) *dst = v;
+          else *dst = f32_to_bf16(v);
+        }
+      }
+}
+
+template <class C, typename OutT, int NM>
+__device__ __forceinline__ void dma_dispatch(int nm, const DmaCtx<C>& t, u16* smem, OutT* O, int N, int lane, int wrow0,
+                                             int wcol0, const TileCoord& tc) {
+  if constexpr (NM <= C::MT) {
+    if (nm == NM) dma_tile<C, OutT, NM>(t, smem, O, N, lane, wrow0, wcol0, tc);
+    else dma_dispatch<C, OutT, NM + 1>(nm, t, smem, O, N, lane, wrow0, wcol0, tc);
+  }
+}
+
+template <class C, typename OutT>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD)))
+void k_gemm_dma(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  extern __shared__ __attribute__((aligned(16))) u16 smem_dma[];
+  int* s_tstart = reinterpret_cast<int*>(smem_dma + 2 * C::STAGE);
+  int* s_goff = s_tstart + (p.n_groups + 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = p.N / BN;
+  const int wrow0 = wm * 16, wcol0 = wn * (BN / WN);
+  build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
+  __syncthreads();
+  const int total = s_tstart[p.n_groups];
+  const TileIter it = tile_range(total);
+  DmaCtx<C> t;
+  t.ar = make_rsrc(p.a, (uint32_t)((size_t)p.a_rows * p.K * 2));
+  t.wave = wave;
+  t.nK = p.K / C::KC;
+  t.lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)smem_dma);
+  const uint32_t w_bytes = (uint32_t)((size_t)p.K * p.N * 2);
+  const uint32_t row_bytes = (uint32_t)p.K * 2;
+  // lane i fills row i / 8 of an 8-row block at chunk position i % 8; the block starts at a row
+  // 8 * (wave + NWAVES * j), so the row's swizzle (row / 2) mod 8 is (i / 16) ^ 4 * (wave & 1)
+  const int q = (lane & 7) ^ (lane >> 4) ^ (4 * (wave & 1));
+  t.b_voff = (uint32_t)(lane >> 3) * row_bytes + q * 16;
+  OutT* O = static_cast<OutT*>(p.out);
+  for (int tile = it.next; tile < it.end; tile += it.step) {
+    const TileCoord tc = tile_coord(s_tstart, s_goff, p.n_groups, tile, BM, BN, tiles_n);
+    const int nm = min(C::MT, max(0, ((tc.rows + 15) / 16 - wm + WM - 1) / WM));
+#pragma unroll
+    for (int m = 0; m < C::NW; ++m)
+      t.wr[m] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)tc.e * w_bytes, w_bytes);
+#pragma unroll
+    for (int j = 0; j < C::A_INST; ++j) {
+      const int r = 8 * (wave + C::NWAVES * j) + (lane >> 3);
+      const int rr = tc.row0 + min(r, tc.rows - 1);
+      int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
+      src = min(max(src, 0), p.a_rows - 1);
+      t.a_voff[j] = r < tc.rows ? (uint32_t)(((size_t)src * p.K + q * 8) * 2) : 0x80000000u;
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_INST; ++j) {
+      const int rb = 8 * (wave + C::NWAVES * j);
+      t.b_m[j] = rb / BN;
+      t.b_soff[j] = (uint32_t)(tc.n0 + rb % BN) * row_bytes;
+    }
+    dma_dispatch<C, OutT, 0>(nm, t, smem_dma, O, p.N, lane, wrow0, wcol0, tc);
+  }
+}
+
+template <class C, typename OutT>
+hipError_t run_dma(const GemmParams& p, hipStream_t s) {
+  if (p.N % C::BN != 0) return hipErrorInvalidValue;   // the caller picks a narrower tile
+  const size_t lds = C::lds_bytes(p.n_groups);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
+  long long grid = device_cu_count();
+  if (grid > max_tiles) grid = max_tiles;
+  grid = ((grid + 7) / 8) * 8;
+  if (grid < 8) grid = 8;
+  k_gemm_dma<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -682,19 +893,23 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
 static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, hipStream_t s) {
   // Tile shapes: rows x columns per tile for gate/up | down, waves, LDS buffers, workgroups per CU.
   //   0 (decode):          32x64   | 32x128,  4 waves (1x4), 1 buffer,  4/CU, two chunks in registers
-  //   1 (prefill):         256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU, one chunk in registers
+  //   1 (prefill):         256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU; dense weights: direct
+  //                        global -> LDS loads; int4: one chunk in registers (dequantised on the way)
   //   2 (prefill, narrow): 256x64  | 256x128, 4 waves (4x1), 2 buffers, 1/CU, two chunks in registers
   const bool n256 = p.N % 256 == 0;
   if (gu) {
     switch (v) {
       case 0: return run_gu<32, 64, 1, 4, 1, 4>(p, q4, s);
-      case 1: return run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, s);
+      case 1: return q4 ? run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, s) : run_dma<DCfg<256, 128, 4, 2, true>, u16>(p, s);
       default: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, s);
     }
   }
   switch (v) {
     case 0: return run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, s);
-    case 1: return n256 ? run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s) : hipErrorInvalidValue;
+    case 1:
+      if (!n256) return hipErrorInvalidValue;
+      if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s);
+      return f32out ? run_dma<DCfg<256, 256, 4, 2, false>, float>(p, s) : run_dma<DCfg<256, 256, 4, 2, false>, u16>(p, s);
     default: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, s);
   }
 }
