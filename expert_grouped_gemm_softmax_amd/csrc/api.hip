@@ -91,7 +91,8 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->op != MOE_OP_GATE_UP_SWIGLU && a->op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
   if (a->act_dtype != MOE_DT_F32 && a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-  if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP) return MOE_ERR_UNSUPPORTED;
+  if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP && a->wfmt != MOE_W_DENSE_NK)
+    return MOE_ERR_UNSUPPORTED;
   const bool gu = a->op == MOE_OP_GATE_UP_SWIGLU;
   if (a->out_dtype != a->act_dtype && !(a->out_dtype == MOE_DT_F32 && !gu)) {
     if (a->out_dtype != MOE_DT_F32 && a->out_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
@@ -116,8 +117,19 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
     if (!a->s0 || (gu && !a->s1)) return MOE_ERR_INVALID_ARG;
   } else if (a->group_size != 0 || a->s0 || a->s1) {
     return MOE_ERR_INVALID_ARG;
+  } else if (a->wfmt == MOE_W_DENSE && a->act_dtype == MOE_DT_BF16) {
+    return MOE_ERR_UNSUPPORTED;                        // prepare with moe_prepare_dense_weights
   }
   return from_hip(moe::launch_grouped_gemm(*a, as_stream(stream)));
+}
+
+MOE_API moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N, int dtype, void* out,
+                                             void* stream) {
+  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E < 1 || K < 1 || N < 1 || E > 65535 || K > (1 << 22) || (long long)E * K * N >= (1LL << 40))
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_prepare(w, E, K, N, dtype, out, as_stream(stream)));
 }
 
 MOE_API moe_status moe_combine(const void* expert_out, int expert_rows, int act_dtype, const int32_t* blob,

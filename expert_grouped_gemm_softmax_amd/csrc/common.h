@@ -37,6 +37,7 @@ hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_
                           int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
                           void* workspace, hipStream_t s);
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s);
+hipError_t launch_prepare(const void* w, int E, int K, int N, int dtype, void* out, hipStream_t s);
 hipError_t launch_combine(const void* o, int act, const int32_t* blob, const int32_t* pair_pos,
                           const void* shared, int T, int k, int H, int rows, void* y,
                           int y_dtype, hipStream_t s);

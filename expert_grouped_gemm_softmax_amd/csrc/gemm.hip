@@ -15,10 +15,10 @@
 //  - Persistent grid, a multiple of 8 workgroups.  Workgroup b runs on XCD b % 8; the tiles are
 //    cut into 8 contiguous ranges and XCD x's workgroups walk range x, so tiles sharing a weight
 //    slab or activation rows share one L2.
-//  - Activation rows are gathered (row_index / row_div) straight into LDS, 16 bytes per lane.
-//  - Activation rows and dense weight rows (W[e][n][k], K-contiguous like a linear layer's
-//    weight) are copied into LDS the same way: 16 bytes per lane, 8 lanes per 128-byte row chunk,
-//    giving [row][k] tiles whose rows are what the MFMA operands read (8 consecutive k per lane).
+//  - Activation rows (gathered through row_index / row_div) and prepared dense weight rows
+//    (W[e][n][k], K-contiguous: MOE_W_DENSE_NK) are copied into LDS the same way: 16 bytes per
+//    lane, 8 lanes per 128-byte row chunk, giving [row][k] tiles whose rows are what the MFMA
+//    operands read (8 consecutive k per lane).
 //    int4 words [e][k/8][n] hold 8 consecutive k of one column: they are dequantised
 //    (q * scale, rounded to bf16) into the same [n][k] LDS layout.
 //  - v_mfma_f32_16x16x32_bf16 with fp32 accumulators; SwiGLU fused in the epilogue (each lane
@@ -732,7 +732,8 @@ hipError_t run_dma(const GemmParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------------------------
 // fp32 kernel (vector ALU): 32 x 64 tiles, K chunks of 32 staged in LDS.
 // ---------------------------------------------------------------------------------------------
-template <bool GU>
+// NK: weights stored [e][n][k] (MOE_W_DENSE_NK), else [e][k][n] (MOE_W_DENSE).
+template <bool GU, bool NK>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
   constexpr int BM = 32, BN = 64, KC = 32, NW = GU ? 2 : 1;
   __shared__ float sA[BM][KC + 1];
@@ -765,10 +766,16 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
         src = min(max(src, 0), p.a_rows - 1);
         sA[r][kk] = A[(size_t)src * p.K + k0 + kk];
       }
-      for (int i = tid; i < NW * KC * BN; i += 256) {
-        const int m = i / (KC * BN), v = i % (KC * BN), n = v / KC, kk = v % KC;
+      for (int i = tid; i < NW * KC * BN; i += 256) {           // consecutive threads: contiguous memory
+        const int m = i / (KC * BN), v = i % (KC * BN);
         const float* W = static_cast<const float*>(m == 0 ? p.w0 : p.w1);
-        sB[m][n][kk] = W[((size_t)e * p.N + n0 + n) * p.K + k0 + kk];
+        if constexpr (NK) {
+          const int n = v / KC, kk = v % KC;
+          sB[m][n][kk] = W[((size_t)e * p.N + n0 + n) * p.K + k0 + kk];
+        } else {
+          const int kk = v / BN, n = v % BN;
+          sB[m][n][kk] = W[((size_t)e * p.K + k0 + kk) * p.N + n0 + n];
+        }
       }
       __syncthreads();
       for (int kk = 0; kk < KC; ++kk) {
@@ -818,7 +825,7 @@ hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool GU>
+template <bool GU, bool NK>
 hipError_t run_f32(const GemmParams& p, hipStream_t s) {
   const size_t lds = 2 * sizeof(int) * (p.n_groups + 1);
   const long long max_tiles = ((long long)(p.rows_cap + 31) / 32 + p.n_groups) * (p.N / 64);
@@ -826,7 +833,7 @@ hipError_t run_f32(const GemmParams& p, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  k_gemm_f32<GU><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
+  k_gemm_f32<GU, NK><<<dim3((unsigned)grid), dim3(256), lds, s>>>(p);
   return hipGetLastError();
 }
 
@@ -878,7 +885,11 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   p.K = a.K; p.N = a.N; p.n_groups = a.n_groups; p.rows_cap = a.rows_cap; p.a_rows = a.a_rows;
   p.row_div = a.row_div; p.group_size = a.group_size > 0 ? a.group_size : a.K;
   const bool gu = a.op == MOE_OP_GATE_UP_SWIGLU;
-  if (a.act_dtype == MOE_DT_F32) return gu ? run_f32<true>(p, s) : run_f32<false>(p, s);
+  if (a.act_dtype == MOE_DT_F32) {
+    const bool nk = a.wfmt == MOE_W_DENSE_NK;
+    return gu ? (nk ? run_f32<true, true>(p, s) : run_f32<true, false>(p, s))
+              : (nk ? run_f32<false, true>(p, s) : run_f32<false, false>(p, s));
+  }
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming

@@ -1,0 +1,45 @@
+// One-time weight preparation for gfx950: dense expert matrices as the layer states them,
+// W[e][k][n] (x·W), are stored transposed as W[e][n][k] -- the [out][in] orientation in which the
+// grouped GEMM reads each output column's K weights as one contiguous row.
+//
+// 64 x 64 tiles through LDS: a workgroup reads 64 rows of 64 consecutive n (coalesced), and
+// writes 64 rows of 64 consecutive k (coalesced); the LDS tile is padded by one element per row so
+// both the row writes and the column reads are free of bank conflicts.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_prepare(const T* __restrict__ w, int K, int N, T* __restrict__ out) {
+  __shared__ T tile[64][64 + 1];
+  const int e = blockIdx.z;
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const T* src = w + (size_t)e * K * N;
+  T* dst = out + (size_t)e * N * K;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
+#pragma unroll
+  for (int r = ty; r < 64; r += 4) {
+    const int k = k0 + r, n = n0 + tx;
+    if (k < K && n < N) tile[r][tx] = src[(size_t)k * N + n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = ty; r < 64; r += 4) {
+    const int n = n0 + r, k = k0 + tx;
+    if (n < N && k < K) dst[(size_t)n * K + k] = tile[tx][r];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const void* w, int E, int K, int N, int dtype, void* out, hipStream_t s) {
+  const dim3 grid((N + 63) / 64, (K + 63) / 64, E), block(256);
+  if (dtype == MOE_DT_BF16)
+    k_prepare<u16><<<grid, block, 0, s>>>(static_cast<const u16*>(w), K, N, static_cast<u16*>(out));
+  else
+    k_prepare<float><<<grid, block, 0, s>>>(static_cast<const float*>(w), K, N, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace moe

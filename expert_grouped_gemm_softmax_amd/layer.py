@@ -15,11 +15,11 @@ from . import _abi, ops
 class ExpertWeights:
     """Device-resident weights of the local experts (and of the optional shared expert).
 
-    Dense ([out][in], the orientation of a linear layer's weight): w_gate, w_up [e_local][I][H],
-    w_down [e_local][H][I] in the activation dtype.
-    int4:  int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N]
-    (K = in, N = out).
-    Shared expert (dense, activation dtype): gate, up [Is][H], down [H][Is]."""
+    A layer weight W is K x N (output n = sum_k a[k] W[k][n]); K = H, N = I for gate/up and the
+    reverse for down.  Dense weights are held prepared, [e_local][N][K] in the activation dtype
+    (MOE_W_DENSE_NK, written by the library from the stated [e_local][K][N]; see upload):
+    w_gate, w_up [e_local][I][H], w_down [e_local][H][I]; shared expert gate, up [Is][H], down [H][Is].
+    int4: int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N]."""
     w_gate: torch.Tensor
     w_up: torch.Tensor
     w_down: torch.Tensor
@@ -44,17 +44,23 @@ def _t(a: np.ndarray, device) -> torch.Tensor:
 
 
 def upload(inputs: dict, cfg, device="cuda") -> tuple[torch.Tensor, torch.Tensor, ExpertWeights]:
-    """Copy a workloads.make_inputs() dict to the GPU -> (x, logits, weights)."""
+    """Copy a workloads.make_inputs() dict to the GPU -> (x, logits, weights).  Dense weights
+    arrive [E][K][N] and are prepared once by the library (moe_prepare_dense_weights)."""
     x = _t(inputs["x"], device)
     logits = _t(inputs["logits"], device)
-    kw = dict(w_gate=_t(inputs["w_gate"], device), w_up=_t(inputs["w_up"], device),
-              w_down=_t(inputs["w_down"], device))
+
+    def dense(name):
+        return ops.prepare_dense_weights(_t(inputs[name], device))
+
     if cfg.wfmt == "int4":
-        kw.update(s_gate=_t(inputs["w_gate_scale"], device), s_up=_t(inputs["w_up_scale"], device),
+        kw = dict(w_gate=_t(inputs["w_gate"], device), w_up=_t(inputs["w_up"], device),
+                  w_down=_t(inputs["w_down"], device),
+                  s_gate=_t(inputs["w_gate_scale"], device), s_up=_t(inputs["w_up_scale"], device),
                   s_down=_t(inputs["w_down_scale"], device), group_size=cfg.group_size)
+    else:
+        kw = dict(w_gate=dense("w_gate"), w_up=dense("w_up"), w_down=dense("w_down"))
     if cfg.shared_I:
-        kw.update(shared_gate=_t(inputs["shared_gate"], device), shared_up=_t(inputs["shared_up"], device),
-                  shared_down=_t(inputs["shared_down"], device))
+        kw.update(shared_gate=dense("shared_gate"), shared_up=dense("shared_up"), shared_down=dense("shared_down"))
     return x, logits, ExpertWeights(**kw)
 
 

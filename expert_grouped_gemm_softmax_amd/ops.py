@@ -98,17 +98,36 @@ def permute(blob: torch.Tensor, e_first: int, e_local: int, sorted_pairs=None, g
     return sp, off, pp
 
 
+def prepare_dense_weights(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Dense weights [E][K][N] (x @ W) -> the same values stored [E][N][K] (MOE_W_DENSE_NK), the
+    layout the bf16 grouped GEMM reads.  A one-time preparation, run by the library."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    E, K, N = w3.shape
+    assert w3.is_contiguous() and w3.dtype in _DT
+    out = out if out is not None else torch.empty((E, N, K), dtype=w.dtype, device=w.device)
+    _dev(w3, out)
+    check("moe_prepare_dense_weights", load().moe_prepare_dense_weights(_ptr(w3), E, K, N, _DT[w.dtype], _ptr(out),
+                                                                        _stream(stream)))
+    return out[0] if squeeze else out
+
+
 def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torch.Tensor,
                  w1: torch.Tensor | None, out: torch.Tensor, *, K: int, N: int, row_index=None,
-                 row_div: int = 1, s0=None, s1=None, group_size: int = 0, m_hint: int = 0, stream=None):
-    """One grouped GEMM (see moe_grouped_gemm in include/moe.h).  Weights are dense
-    [n_groups][N][K] in the activation dtype, or int32 int4 words [n_groups][K/8][N] with bf16
-    scales s0/s1 [n_groups][K/group_size][N]."""
+                 row_div: int = 1, s0=None, s1=None, group_size: int = 0, m_hint: int = 0,
+                 weights_nk: bool = True, stream=None):
+    """One grouped GEMM (see moe_grouped_gemm in include/moe.h).  Dense weights are
+    [n_groups][N][K] (weights_nk, from prepare_dense_weights) or [n_groups][K][N] (fp32 only) in the
+    activation dtype; int4 weights are int32 words [n_groups][K/8][N] with bf16 scales s0/s1
+    [n_groups][K/group_size][N]."""
     _dev(a, group_offsets, w0, w1, out, row_index, s0, s1)
     args = _abi.MoeGemmArgs()
     args.op = op
     args.act_dtype = _DT[a.dtype]
-    args.wfmt = _abi.MOE_W_INT4_SYM_GROUP if w0.dtype == torch.int32 else _abi.MOE_W_DENSE
+    if w0.dtype == torch.int32:
+        args.wfmt = _abi.MOE_W_INT4_SYM_GROUP
+    else:
+        args.wfmt = _abi.MOE_W_DENSE_NK if weights_nk else _abi.MOE_W_DENSE
     args.group_size = group_size if args.wfmt == _abi.MOE_W_INT4_SYM_GROUP else 0
     args.K, args.N = K, N
     args.n_groups = group_offsets.numel() - 1

@@ -138,12 +138,8 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     optional Zipf bias zipf_bias * ln(1/rank) with rank(e) = e + 1 (or a seeded random rank
     permutation), plus optional rounding to multiples of `tie_quantum` to inject ties.
 
-    A weight matrix W (output n = sum_k a[k] W[k][n], K = fan_in) is stored dense as [N][K]
-    (row n holds the weights of output n, a linear layer's [out][in] orientation) and drawn in
-    that shape; int4 weights are drawn as [K][N], quantised along K and packed into int32 words
-    [e][K/8][N] with uint16 bf16 scales [e][K/gs][N].
-
-    Returns a dict of numpy arrays (bf16 tensors are uint16 bit patterns).
+    Returns a dict of numpy arrays (bf16 tensors are uint16 bit patterns, int4 weights are
+    int32 words [e][K/8][N] with uint16 bf16 scales [e][K/gs][N]).
     """
     T, H, E, I, el = cfg.T, cfg.H, cfg.E, cfg.I, cfg.e_local
     ss = np.random.SeedSequence(cfg.seed).spawn(2 + 3 * el + 3)
@@ -173,14 +169,15 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     out["logits"] = np.ascontiguousarray(logits, dtype=np.float32)
 
     def one(args):
-        seed, K, N = args
+        seed, shape, fan_in = args
+        w = _normal(seed, shape, 1.0 / math.sqrt(fan_in))
         if cfg.wfmt == "int4":
-            q, s_bits = quantize_int4_sym(_normal(seed, (K, N), 1.0 / math.sqrt(K)), cfg.group_size)
+            q, s_bits = quantize_int4_sym(w, cfg.group_size)
             return pack_int4(q), s_bits
-        w = _normal(seed, (N, K), 1.0 / math.sqrt(K))
         return f32_to_bf16_bits(w) if bf16 else w
 
-    jobs = [(s, H, I) for s in s_g] + [(s, H, I) for s in s_u] + [(s, I, H) for s in s_d]
+    jobs = ([(s, (H, I), H) for s in s_g] + [(s, (H, I), H) for s in s_u] +
+            [(s, (I, H), I) for s in s_d])
     with ThreadPoolExecutor(max(1, threads)) as ex:
         res = list(ex.map(one, jobs))
     names = ("w_gate", "w_up", "w_down")
@@ -193,8 +190,8 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
             out[name] = np.stack(part)
     if cfg.shared_I:
         Is = cfg.shared_I
-        sh = [(s_sh[0], H, Is), (s_sh[1], H, Is), (s_sh[2], Is, H)]
-        for name, (seed, K, N) in zip(("shared_gate", "shared_up", "shared_down"), sh):
-            w = _normal(seed, (N, K), 1.0 / math.sqrt(K))
+        sh = [(s_sh[0], (H, Is), H), (s_sh[1], (H, Is), H), (s_sh[2], (Is, H), Is)]
+        for name, (seed, shape, fan_in) in zip(("shared_gate", "shared_up", "shared_down"), sh):
+            w = _normal(seed, shape, 1.0 / math.sqrt(fan_in))
             out[name] = f32_to_bf16_bits(w) if bf16 else w
     return out

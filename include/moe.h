@@ -47,14 +47,18 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
 
-/* Expert weight formats.  MOE_W_INT4_SYM_GROUP: symmetric int4 with one bf16 scale per group of
+/* Expert weight formats for a K x N matrix W of expert e (output n = sum_k a[k] W[k][n]).
+ * MOE_W_DENSE: W[e][k][n] in the activation dtype, the layout the layer is stated in.
+ * MOE_W_DENSE_NK: the same values stored [e][n][k] (row n = the K weights of output n), as
+ * moe_prepare_dense_weights writes them; the bf16 grouped GEMM reads this layout.
+ * MOE_W_INT4_SYM_GROUP: symmetric int4 with one bf16 scale per group of
  * `group_size` consecutive K rows per output column ("vLLM TPU Inference v0.31.0", 4-bit weight
  * scope: symmetric int4, group-wise scales, activations not quantised; asymmetric, 8-bit and
  * activation-order variants are not supported there and are not representable here).
  * Layout for a [K][N] matrix of expert e: words int32 [E][K/8][N], the two's-complement nibble at
  * bits 4i..4i+3 of word [e][kb][n] is q[8*kb+i][n]; scales bf16 [E][K/group_size][N];
  * weight = q * scale.  Channel-wise scales are group_size == K. */
-typedef enum moe_wfmt { MOE_W_DENSE = 0, MOE_W_INT4_SYM_GROUP = 1 } moe_wfmt;
+typedef enum moe_wfmt { MOE_W_DENSE = 0, MOE_W_INT4_SYM_GROUP = 1, MOE_W_DENSE_NK = 2 } moe_wfmt;
 
 typedef enum moe_gemm_op {
   MOE_OP_GATE_UP_SWIGLU = 0,  /* out = silu(A Wg) * (A Wu), silu(z) = z / (1 + e^-z) */
@@ -138,8 +142,9 @@ moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_loc
  * A row a[row_index[r] / row_div] (or a[r] when row_index is NULL) and expert e's weights.
  * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg(e)[k][n]) * (sum_k A[k] Wu(e)[k][n]).
  * DOWN:           out[r][n] = sum_k A[k] Wd(e)[k][n].
- * W(e)[k][n] is stored as w[e][n][k] for dense weights (row n holds the K weights of output n,
- * the [out][in] orientation of a linear layer) and as nibble k%8 of word [e][k/8][n] for int4.
+ * Weight formats: bf16 activations take MOE_W_DENSE_NK (prepare MOE_W_DENSE weights once with
+ * moe_prepare_dense_weights; MOE_W_DENSE itself is MOE_ERR_UNSUPPORTED there) or
+ * MOE_W_INT4_SYM_GROUP; fp32 activations take MOE_W_DENSE or MOE_W_DENSE_NK.
  * bf16 path: bf16 operands, fp32 accumulation, bf16 or (DOWN) fp32 output; int4 weights are
  * dequantised to bf16 in LDS.  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are
  * not written.  Limits (32-bit byte offsets): a_rows * K * sizeof(act) < 2^31 and
@@ -163,7 +168,7 @@ typedef struct moe_gemm_args {
   const void* a;                 /* [a_rows][K] act dtype */
   const int32_t* row_index;      /* [rows_cap] (e.g. sorted_pairs) or NULL for identity rows */
   const int32_t* group_offsets;  /* [n_groups+1] non-decreasing, [0] = 0 (e.g. from moe_permute) */
-  const void* w0;      /* GATE_UP: Wg; DOWN: Wd.  Dense [n_groups][N][K]; int4 words [n_groups][K/8][N] */
+  const void* w0;      /* GATE_UP: Wg; DOWN: Wd, in format wfmt (see moe_wfmt) */
   const void* w1;      /* GATE_UP: Wu (same layout as w0); DOWN: NULL */
   const void* s0;      /* int4: bf16 scales of w0 [n_groups][K/group_size][N]; dense: NULL */
   const void* s1;      /* int4: bf16 scales of w1; otherwise NULL */
@@ -171,6 +176,14 @@ typedef struct moe_gemm_args {
 } moe_gemm_args;
 
 moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
+
+/*
+ * moe_prepare_dense_weights -- one-time weight preparation (not part of the per-batch path):
+ * out[e][n][k] = w[e][k][n] for E matrices of K x N in dtype (MOE_DT_F32 or MOE_DT_BF16), i.e.
+ * MOE_W_DENSE -> MOE_W_DENSE_NK.  w and out must not overlap.
+ *   Limits: 1 <= E <= 65535, 1 <= K <= 2^22, 1 <= N, E * K * N < 2^40.
+ */
+moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N, int dtype, void* out, void* stream);
 
 /*
  * moe_combine -- weighted sum back to token order ("Systems engineering playbook ...",

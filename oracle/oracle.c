@@ -28,8 +28,6 @@
  *    group-wise scales, only the needed tiles restored on chip.  Reading taken here: word
  *    [e][K/8][N] int32, two's-complement nibble i (bits 4i..4i+3) holds K-row 8*kb+i, bf16
  *    scales [e][K/gs][N]; the oracle dequantises exactly (q * s in double).
- *  - Dense weight storage (the pages give none): [e][N][K], row n holding the K weights that
- *    feed output n, the [out][in] orientation of a linear layer's weight matrix.
  *
  * All FFN arithmetic is in double from exactly converted inputs; nothing is rounded to bf16.
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math): the routing sequence relies on
@@ -186,65 +184,53 @@ int orc_int4_nibble(int32_t word, int i) {
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_DENSE = 0, ORC_INT4 = 1 };
 
-/* Matrix e of a stack of K x N weight matrices W (output n = sum_k a[k] W[k][n]). */
+/* Row kk of matrix `e` of a stack of [K][N] matrices, converted exactly to double. */
 typedef struct {
-  const void* w;            /* dense: f32/bf16 stored [E][N][K]; int4: int32 words [E][K/8][N] */
+  const void* w;            /* dense: f32/bf16 [E][K][N]; int4: int32 words [E][K/8][N] */
   const uint16_t* scale;    /* int4 only: bf16 [E][K/gs][N] */
   int fmt, act, K, N, gs;
 } orc_mat;
 
-/* The K weights W[0..K-1][n] of output n of matrix e, converted exactly to double. */
-static void orc_col(const orc_mat* m, int e, int n, double* out) {
-  const size_t K = (size_t)m->K, N = (size_t)m->N;
+static void orc_row(const orc_mat* m, int e, int kk, double* out) {
+  const size_t N = (size_t)m->N;
   if (m->fmt == ORC_INT4) {
-    const int32_t* words = (const int32_t*)m->w + (size_t)e * (K / 8) * N + n;
-    const uint16_t* s = m->scale + (size_t)e * (K / m->gs) * N + n;
-    for (size_t kk = 0; kk < K; ++kk)
-      out[kk] = (double)orc_int4_nibble(words[(kk / 8) * N], (int)(kk % 8)) * orc_bf16_to_double(s[(kk / m->gs) * N]);
+    const int32_t* words = (const int32_t*)m->w + ((size_t)e * (m->K / 8) + kk / 8) * N;
+    const uint16_t* s = m->scale + ((size_t)e * (m->K / m->gs) + kk / m->gs) * N;
+    for (size_t n = 0; n < N; ++n)
+      out[n] = (double)orc_int4_nibble(words[n], kk % 8) * orc_bf16_to_double(s[n]);
   } else if (m->act == ORC_BF16) {
-    const uint16_t* r = (const uint16_t*)m->w + ((size_t)e * N + n) * K;
-    for (size_t kk = 0; kk < K; ++kk) out[kk] = orc_bf16_to_double(r[kk]);
+    const uint16_t* r = (const uint16_t*)m->w + ((size_t)e * m->K + kk) * N;
+    for (size_t n = 0; n < N; ++n) out[n] = orc_bf16_to_double(r[n]);
   } else {
-    const float* r = (const float*)m->w + ((size_t)e * N + n) * K;
-    for (size_t kk = 0; kk < K; ++kk) out[kk] = (double)r[kk];
+    const float* r = (const float*)m->w + ((size_t)e * m->K + kk) * N;
+    for (size_t n = 0; n < N; ++n) out[n] = (double)r[n];
   }
 }
 
-/* Dequantise (or convert) matrix e of a stack to double [K][N] (out[k*N + n] = W[k][n]). */
+/* Dequantise (or convert) matrix e of a stack to double [K][N]. */
 void orc_expand_matrix(const void* w, const uint16_t* scale, int fmt, int act, int K, int N, int gs,
                        int e, double* out) {
   orc_mat m = {w, scale, fmt, act, K, N, gs};
-  double* col = (double*)malloc(sizeof(double) * (size_t)K);
-  for (int n = 0; n < N; ++n) {
-    orc_col(&m, e, n, col);
-    for (int kk = 0; kk < K; ++kk) out[(size_t)kk * N + n] = col[kk];
-  }
-  free(col);
-}
-
-/* sum_k a[k] * col[k] in ascending k. */
-static double orc_dot(const double* a, const double* col, int K) {
-  double s = 0.0;
-  for (int kk = 0; kk < K; ++kk) s += a[kk] * col[kk];
-  return s;
+  for (int kk = 0; kk < K; ++kk) orc_row(&m, e, kk, out + (size_t)kk * N);
 }
 
 static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* One SwiGLU expert on one input row a[H] (double): out[H] = (silu(a Wg) * (a Wu)) Wd.
- * gacc/uacc hold a Wg and a Wu, then h = silu(a Wg) * (a Wu) in gacc. */
+/* One SwiGLU expert on one input row a[H] (double): out[H] = (silu(a Wg) * (a Wu)) Wd. */
 static void orc_swiglu(const double* a, const orc_mat* g, const orc_mat* u, const orc_mat* d,
-                       int e, int H, int I, double* gacc, double* uacc, double* col, double* out) {
-  for (int n = 0; n < I; ++n) {
-    orc_col(g, e, n, col);
-    gacc[n] = orc_dot(a, col, H);
-    orc_col(u, e, n, col);
-    uacc[n] = orc_dot(a, col, H);
+                       int e, int H, int I, double* gacc, double* uacc, double* row, double* out) {
+  for (int n = 0; n < I; ++n) { gacc[n] = 0.0; uacc[n] = 0.0; }
+  for (int kk = 0; kk < H; ++kk) {
+    orc_row(g, e, kk, row);
+    for (int n = 0; n < I; ++n) gacc[n] += a[kk] * row[n];
+    orc_row(u, e, kk, row);
+    for (int n = 0; n < I; ++n) uacc[n] += a[kk] * row[n];
   }
-  for (int i = 0; i < I; ++i) gacc[i] = orc_silu(gacc[i]) * uacc[i];
-  for (int n = 0; n < H; ++n) {
-    orc_col(d, e, n, col);
-    out[n] = orc_dot(gacc, col, I);
+  for (int n = 0; n < H; ++n) out[n] = 0.0;
+  for (int i = 0; i < I; ++i) {
+    double h = orc_silu(gacc[i]) * uacc[i];
+    orc_row(d, e, i, row);
+    for (int n = 0; n < H; ++n) out[n] += h * row[n];
   }
 }
 
@@ -257,9 +243,9 @@ typedef struct {
   const void* x;    /* [T][H] */
   const int32_t* ids;   /* [T][k] global expert ids */
   const float* w;       /* [T][k] routing weights */
-  const void* wg; const void* wu; const void* wd;       /* K x N matrices per expert: H x I, H x I, I x H */
+  const void* wg; const void* wu; const void* wd;       /* [e_local][H][I], [e_local][H][I], [e_local][I][H] */
   const uint16_t* sg; const uint16_t* su; const uint16_t* sd;   /* int4 scales */
-  const void* shg; const void* shu; const void* shd;    /* shared dense H x Is, H x Is, Is x H */
+  const void* shg; const void* shu; const void* shd;    /* shared [H][Is], [H][Is], [Is][H] */
 } orc_layer_args;
 
 /* y[i][:] (double [n_tokens][H]) for token tokens[i]: the routed-expert combine over the
@@ -271,7 +257,7 @@ void orc_layer(const orc_layer_args* A, const int32_t* tokens, int n_tokens, dou
   double* a = (double*)malloc(sizeof(double) * (size_t)H);
   double* gacc = (double*)malloc(sizeof(double) * (size_t)Imax);
   double* uacc = (double*)malloc(sizeof(double) * (size_t)Imax);
-  double* col = (double*)malloc(sizeof(double) * (size_t)wide);
+  double* row = (double*)malloc(sizeof(double) * (size_t)wide);
   double* o = (double*)malloc(sizeof(double) * (size_t)H);
   orc_mat g = {A->wg, A->sg, A->wfmt, A->act, H, I, A->group_size};
   orc_mat u = {A->wu, A->su, A->wfmt, A->act, H, I, A->group_size};
@@ -291,13 +277,13 @@ void orc_layer(const orc_layer_args* A, const int32_t* tokens, int n_tokens, dou
       const int id = A->ids[(size_t)t * k + j];
       if (id < A->e_first || id >= A->e_first + A->e_local) continue;
       const double wj = (double)A->w[(size_t)t * k + j];
-      orc_swiglu(a, &g, &u, &d, id - A->e_first, H, I, gacc, uacc, col, o);
+      orc_swiglu(a, &g, &u, &d, id - A->e_first, H, I, gacc, uacc, row, o);
       for (int n = 0; n < H; ++n) yt[n] += wj * o[n];
     }
     if (A->shared_I > 0) {
-      orc_swiglu(a, &sg, &su, &sd, 0, H, A->shared_I, gacc, uacc, col, o);
+      orc_swiglu(a, &sg, &su, &sd, 0, H, A->shared_I, gacc, uacc, row, o);
       for (int n = 0; n < H; ++n) yt[n] += o[n];
     }
   }
-  free(o); free(col); free(uacc); free(gacc); free(a);
+  free(o); free(row); free(uacc); free(gacc); free(a);
 }

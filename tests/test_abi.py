@@ -98,7 +98,7 @@ def test_pack_and_permute_validation(L):
 
 def _gemm(**kw):
     a = MoeGemmArgs()
-    base = dict(op=0, act_dtype=1, wfmt=0, group_size=0, K=256, N=128, n_groups=8, rows_cap=64,
+    base = dict(op=0, act_dtype=1, wfmt=2, group_size=0, K=256, N=128, n_groups=8, rows_cap=64,
                 a_rows=32, row_div=2, m_hint=0, out_dtype=1, a=FAKE, row_index=FAKE, group_offsets=FAKE,
                 w0=FAKE, w1=FAKE, s0=None, s1=None, out=FAKE)
     base.update(kw)
@@ -109,6 +109,7 @@ def _gemm(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(op=2), INV), (dict(act_dtype=7), UNS), (dict(wfmt=5), UNS), (dict(out_dtype=0), INV),
+    (dict(wfmt=0), UNS),                      # bf16 GEMM reads prepared (MOE_W_DENSE_NK) weights
     (dict(out_dtype=4), UNS), (dict(act_dtype=0, out_dtype=1), INV),
     (dict(a=None), INV), (dict(group_offsets=None), INV), (dict(w0=None), INV), (dict(out=None), INV),
     (dict(w1=None), INV), (dict(op=1, K=128, N=256, w1=FAKE), INV), (dict(K=32), INV), (dict(K=96), INV),
@@ -142,3 +143,16 @@ def test_combine_validation(L):
         args = list(ok)
         args[i] = v
         assert L.moe_combine(*args) == UNS, (i, v)
+
+
+def test_prepare_dense_weights_validation(L):
+    F = FAKE
+    assert L.moe_prepare_dense_weights(None, 2, 64, 64, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 2, 64, 64, 1, None, None) == INV
+    assert L.moe_prepare_dense_weights(F, 2, 64, 64, 7, F, None) == UNS
+    assert L.moe_prepare_dense_weights(F, 0, 64, 64, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 2, 0, 64, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 2, 64, 0, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 65536, 64, 64, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 1, (1 << 22) + 1, 64, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 1024, 1 << 15, 1 << 15, 1, F, None) == INV   # 2^40 elements

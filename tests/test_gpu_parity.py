@@ -134,6 +134,35 @@ def test_route_packed_equals_route_then_pack(T, E, k):
     assert torch.equal(blob, blob2) and torch.equal(blob, blob3)
 
 
+@pytest.mark.parametrize("E,K,N,dt", [(1, 64, 64, torch.bfloat16), (3, 4096, 1024, torch.bfloat16),
+                                       (2, 1024, 4096, torch.bfloat16), (5, 100, 37, torch.float32),
+                                       (1, 1, 1, torch.float32)])
+def test_prepare_dense_weights_is_a_transpose(E, K, N, dt):
+    g = torch.Generator().manual_seed(E * K + N)
+    w = torch.randn((E, K, N), generator=g).to(dt).to(_dev())
+    out = ops.prepare_dense_weights(w)
+    torch.cuda.synchronize()
+    ref = w.transpose(1, 2).contiguous()
+    assert out.shape == (E, N, K) and torch.equal(out.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                                                   ref.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+
+
+def test_fp32_gemm_reads_both_dense_layouts_identically():
+    cfg = MID["f32"]
+    inp = W.make_inputs(cfg)
+    x, logits, wts = upload(inp, cfg, _dev())
+    layer = MoELayer.from_config(cfg, wts)
+    layer.forward(x, logits)
+    b = layer.buffers(cfg.T, _dev())
+    wg, wu = (torch.from_numpy(inp[n]).to(_dev()) for n in ("w_gate", "w_up"))      # stated [E][K][N]
+    h2 = torch.empty_like(b.h)
+    ops.grouped_gemm(0, x, b.group_offsets, wg, wu, h2, K=cfg.H, N=cfg.I, row_index=b.sorted_pairs,
+                     row_div=cfg.k, weights_nk=False)
+    torch.cuda.synchronize()
+    n = int(b.group_offsets[-1])
+    assert torch.equal(h2[:n].view(torch.int32), b.h[:n].view(torch.int32))
+
+
 def test_permute_with_no_local_pair():
     T, k = 50, 4
     ids = np.stack([np.arange(100, 104)] * T).astype(np.int32)

@@ -199,8 +199,6 @@ def test_permute_is_stable_counting_sort(T, k, E, e_first, e_local):
 # Expert FFN and combine
 # ----------------------------------------------------------------------------------------------
 def _dense_f64(inp, cfg, name):
-    """Input `name` as float64; a weight matrix comes back as W[K][N] (output = x @ W), from
-    dense storage [N][K] or from int4 words [K/8][N]."""
     a = inp[name]
     if cfg.wfmt == "int4" and name in ("w_gate", "w_up", "w_down"):
         words = a.view(np.uint32)
@@ -211,8 +209,9 @@ def _dense_f64(inp, cfg, name):
             q[:, i::8, :] = np.where(nib >= 8, nib - 16, nib)
         s = W.bf16_bits_to_f32(inp[name + "_scale"]).astype(np.float64)
         return q * np.repeat(s, cfg.group_size, axis=1)
-    f = W.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
-    return f if name == "x" else np.swapaxes(f, -1, -2)
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def _silu(z):
@@ -270,7 +269,7 @@ def test_layer_identical_experts_reduce_to_one_ffn():
     ids, w = oracle.route(inp["logits"], cfg.k)
     y = oracle.layer(inp, cfg, ids, w)
     x = inp["x"].astype(np.float64)
-    ffn = (_silu(x @ inp["w_gate"][0].T) * (x @ inp["w_up"][0].T)) @ inp["w_down"][0].T
+    ffn = (_silu(x @ inp["w_gate"][0]) * (x @ inp["w_up"][0])) @ inp["w_down"][0]
     # the weights sum to one within k fp32 roundings
     assert np.abs(y - ffn).max() <= cfg.k * 2.0 ** -23 * np.abs(ffn).max() * 4
 
@@ -284,8 +283,7 @@ def test_layer_single_expert_is_textbook_swiglu_mlp():
     y = oracle.layer(inp, cfg, ids, w)
     x = torch.from_numpy(inp["x"].astype(np.float64))
     g, u, d = (torch.from_numpy(inp[n][0].astype(np.float64)) for n in ("w_gate", "w_up", "w_down"))
-    F = torch.nn.functional                     # [out][in] weights, as torch's linear layers store them
-    ref = F.linear(F.silu(F.linear(x, g)) * F.linear(x, u), d)
+    ref = (torch.nn.functional.silu(x @ g) * (x @ u)) @ d
     assert np.allclose(y, ref.numpy(), rtol=1e-13, atol=1e-14)
 
 
@@ -303,7 +301,7 @@ def test_layer_zero_and_scaled_down_projection():
     inp0 = dict(inp, w_down=np.zeros_like(inp["w_down"]))
     y0 = oracle.layer(inp0, cfg, ids, w)
     x = inp["x"].astype(np.float64)
-    sh = (_silu(x @ inp["shared_gate"].T) * (x @ inp["shared_up"].T)) @ inp["shared_down"].T
+    sh = (_silu(x @ inp["shared_gate"]) * (x @ inp["shared_up"])) @ inp["shared_down"]
     assert np.allclose(y0, sh, rtol=1e-13, atol=1e-15)
     assert np.allclose(base - y0, y1, rtol=1e-12, atol=1e-13)
 
