@@ -10,6 +10,8 @@
  *   4. moe_grouped_gemm  per-expert SwiGLU FFN: fused gate/up projection + SwiGLU, then the down
  *                        projection, with bf16 or symmetric int4 group-quantised (W4A16) weights;
  *   5. moe_combine       weighted sum of each token's expert outputs back in token order.
+ * Also: moe_route_packed (steps 1 and 2 in one launch) and moe_prepare_dense_weights (one-time,
+ * load-time storage of dense expert weights in the layout the bf16 grouped GEMM reads).
  *
  * Conventions shared by every entry point:
  *   - Every array argument is a DEVICE pointer owned by the caller.  The library never allocates,
