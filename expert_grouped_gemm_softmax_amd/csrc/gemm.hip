@@ -758,24 +758,39 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
     const int mt = local % mtiles, nt = local / mtiles;
     const int row0 = g0 + mt * BM, rows = min(BM, g1 - row0), n0 = nt * BN;
     float acc[NW][2][4] = {};
+    // source rows of this thread's activation elements (fixed for the tile)
+    constexpr int A_PER = BM * KC / 256, B_PER = NW * KC * BN / 256;
+    const float* a_src[A_PER];
+#pragma unroll
+    for (int u = 0; u < A_PER; ++u) {
+      const int r = (tid + 256 * u) / KC;
+      const int rr = row0 + min(r, rows - 1);
+      int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
+      src = min(max(src, 0), p.a_rows - 1);
+      a_src[u] = A + (size_t)src * p.K + (tid + 256 * u) % KC;
+    }
     for (int k0 = 0; k0 < p.K; k0 += KC) {
-      for (int i = tid; i < BM * KC; i += 256) {
-        const int r = i / KC, kk = i % KC;
-        const int rr = row0 + min(r, rows - 1);
-        int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
-        src = min(max(src, 0), p.a_rows - 1);
-        sA[r][kk] = A[(size_t)src * p.K + k0 + kk];
-      }
-      for (int i = tid; i < NW * KC * BN; i += 256) {           // consecutive threads: contiguous memory
+      // all loads of the chunk are issued before the first LDS store (consecutive threads read
+      // contiguous memory)
+      float av[A_PER], bv[B_PER];
+#pragma unroll
+      for (int u = 0; u < A_PER; ++u) av[u] = a_src[u][k0];
+#pragma unroll
+      for (int u = 0; u < B_PER; ++u) {
+        const int i = tid + 256 * u;
         const int m = i / (KC * BN), v = i % (KC * BN);
         const float* W = static_cast<const float*>(m == 0 ? p.w0 : p.w1);
-        if constexpr (NK) {
-          const int n = v / KC, kk = v % KC;
-          sB[m][n][kk] = W[((size_t)e * p.N + n0 + n) * p.K + k0 + kk];
-        } else {
-          const int kk = v / BN, n = v % BN;
-          sB[m][n][kk] = W[((size_t)e * p.K + k0 + kk) * p.N + n0 + n];
-        }
+        if constexpr (NK) bv[u] = W[((size_t)e * p.N + n0 + v / KC) * p.K + k0 + v % KC];
+        else bv[u] = W[((size_t)e * p.K + k0 + v / BN) * p.N + n0 + v % BN];
+      }
+#pragma unroll
+      for (int u = 0; u < A_PER; ++u) sA[(tid + 256 * u) / KC][(tid + 256 * u) % KC] = av[u];
+#pragma unroll
+      for (int u = 0; u < B_PER; ++u) {
+        const int i = tid + 256 * u;
+        const int m = i / (KC * BN), v = i % (KC * BN);
+        if constexpr (NK) sB[m][v / KC][v % KC] = bv[u];
+        else sB[m][v % BN][v / BN] = bv[u];
       }
       __syncthreads();
       for (int kk = 0; kk < KC; ++kk) {
