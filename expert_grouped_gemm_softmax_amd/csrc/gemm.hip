@@ -126,6 +126,8 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // ---------------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------------------------
+constexpr size_t kLdsPerCu = 160 * 1024;             // LDS of one gfx950 compute unit
+
 // Raw buffer resource (gfx9 family dword 3): weight loads use one scalar descriptor per tile
 // plus 32-bit per-lane byte offsets.
 constexpr int kBufferWord3 = 0x00020000;
@@ -719,7 +721,7 @@ template <class C, typename OutT>
 hipError_t run_dma(const GemmParams& p, hipStream_t s) {
   if (p.N % C::BN != 0) return hipErrorInvalidValue;   // the caller picks a narrower tile
   const size_t lds = C::lds_bytes(p.n_groups);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if (lds > kLdsPerCu) return hipErrorInvalidValue;
   const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
   long long grid = device_cu_count();
   if (grid > max_tiles) grid = max_tiles;
@@ -821,7 +823,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
   }
 }
 
-constexpr size_t kLdsPerCu = 160 * 1024;
 
 template <class C, typename OutT>
 hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
