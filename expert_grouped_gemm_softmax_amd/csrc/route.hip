@@ -7,8 +7,8 @@
 //
 // One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers as
 // 64-bit selection keys (logit order, then lower expert id), sorted once per lane; each of the k
-// rounds is a 4-step DPP max of the lane heads inside each 16-lane row and a max of the four row
-// winners read with v_readlane.  The weights need no E-term reduction: slot j's
+// rounds is a 6-step DPP max of the lane heads (4 steps inside each 16-lane row, 2 row broadcasts)
+// read from lane 63 with v_readlane.  The weights need no E-term reduction: slot j's
 // weight only involves the k selected logits.
 #include "common.h"
 
@@ -57,13 +57,16 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 }
 __device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
 
-// DPP controls (gfx9 encoding): quad permutations, reverse within 8 lanes, reverse within 16.
+// DPP controls (gfx9 encoding): quad permutations, reverse within 8 lanes, reverse within 16,
+// and the wave64 row broadcasts of lane 15 (to the next row) and lane 31 (to rows 2 and 3).
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
-template <int CTRL>
+// max(k, k of the DPP source lane); lanes outside ROW_MASK keep k (their DPP result is the key 0).
+template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROW_MASK, 0xf, false);
   const uint64_t o = ((uint64_t)hi << 32) | lo;
   return o > k ? o : k;
 }
@@ -108,13 +111,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
     m = dpp_max<kQuadXor2>(m);
     m = dpp_max<kRowHalfMirror>(m);
     m = dpp_max<kRowMirror>(m);
-    // largest of the four rows (wave-uniform)
-    uint64_t best = readlane64(m, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-      const uint64_t o = readlane64(m, r);
-      best = o > best ? o : best;
-    }
+    // rows 1 and 3 take the max with rows 0 and 2, then row 3 with row 1: lane 63 holds the largest
+    m = dpp_max<kRowBcast15, 0xa>(m);
+    m = dpp_max<kRowBcast31, 0xc>(m);
+    const uint64_t best = readlane64(m, 63);          // wave-uniform
     if (key[0] == best) {                                 // the winner's list advances
 #pragma unroll
       for (int i = 0; i + 1 < PER_LANE; ++i) key[i] = key[i + 1];
