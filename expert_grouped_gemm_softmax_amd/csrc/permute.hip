@@ -27,6 +27,8 @@ constexpr int kChunk = kWavesPerChunk * kWavePairs;        // 512 pairs per work
 constexpr int kSmallWaves = 16;                            // single-workgroup path
 constexpr int kSmallSteps = 16;                            // 64-pair steps per wavefront at most
 constexpr int kSmallPairs = kSmallWaves * kSmallSteps * 64;   // 16384
+constexpr int kBitsMaxExperts = 64;                       // token-bit path: one lane per expert
+constexpr int kBitsMaxWords = 64;                         // and at most 2048 tokens
 
 __device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
   uint64_t same = __ballot(valid);
@@ -36,6 +38,19 @@ __device__ __forceinline__ uint64_t match_local(int le, bool valid, int nbits) {
     same &= bit ? bb : ~bb;
   }
   return same;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront: four row shifts inside each 16-lane row,
+// then the row broadcasts of lanes 15 and 31 (lanes whose DPP source is outside the row or whose
+// row is masked off add 0).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return x;
 }
 
 // Local expert id of pair p (-1 outside [0, e_local) or p >= end).
@@ -176,12 +191,7 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
         }
       }
     }
-    int incl = total;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
+    const int incl = wave_incl_scan(total);
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
     int wave_base = 0;
@@ -227,16 +237,30 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
 }
 
 // Whole permutation in one workgroup of kSmallWaves wavefronts; wavefront w owns the consecutive
-// pairs [w * span, (w + 1) * span), span a multiple of 64.  Pass 1 counts per wavefront, the
-// offsets and per-wavefront row bases come from one scan over the experts, pass 2 recounts in the
-// same order and writes the rows.
-__global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* __restrict__ blob, int P,
+// pairs [w * span, (w + 1) * span), span a multiple of 64.
+//
+// Token-bit path (words > 0: at most 64 local experts and 32 * words >= T tokens): bit t of row e
+// of an LDS bit matrix is set when token t has a pair routed to local expert e.  When no token
+// routes two of its pairs to one expert (the bit was never set twice), the rank of pair (t, e)
+// inside group e is the number of bits of row e below t: one wavefront turns the rows into
+// per-word prefix counts and the group offsets (one lane per expert), and every pair then finds
+// its row with three LDS reads.  Stable order within a group is ascending token, which is
+// ascending pair index.
+//
+// Otherwise (or if some token repeats an expert): pass 1 counts per wavefront with the match-any
+// ballots, the offsets and per-wavefront row bases come from one scan over the experts, pass 2
+// recounts in the same order and writes the rows.
+__global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* __restrict__ blob, int P, int k,
                                                                  int e_first, int e_local, int nbits, int span,
-                                                                 int32_t* __restrict__ sorted_pairs,
+                                                                 int words, int32_t* __restrict__ sorted_pairs,
                                                                  int32_t* __restrict__ group_offsets,
                                                                  int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t lds[];                         // [kSmallWaves][e_local] counts -> row bases
   int32_t* wsum = lds + kSmallWaves * e_local;             // [kSmallWaves]
+  uint32_t* bits = reinterpret_cast<uint32_t*>(wsum + kSmallWaves);   // [words][64]
+  int32_t* pre = reinterpret_cast<int32_t*>(bits + words * 64);       // [words][64] bits of row e below word w
+  int32_t* goff = pre + words * 64;                        // [64] group offsets
+  int32_t* repeat = goff + 64;                             // [1] some token repeats an expert
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int beg = wv * span, end = min(P, beg + span);
   // all of this wavefront's ids in registers, loaded at once (span <= 64 * kSmallSteps)
@@ -244,7 +268,60 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* 
 #pragma unroll
   for (int u = 0; u < kSmallSteps; ++u) le[u] = local_id(blob, beg + 64 * u + lane, end, e_first, e_local);
   for (int i = threadIdx.x; i < kSmallWaves * e_local; i += blockDim.x) lds[i] = 0;
+  for (int i = threadIdx.x; i < words * 64; i += blockDim.x) bits[i] = 0u;
+  if (threadIdx.x == 0) *repeat = 0;
   __syncthreads();
+
+  if (words > 0) {
+    bool rep = false;
+#pragma unroll
+    for (int u = 0; u < kSmallSteps; ++u) {
+      if (beg + 64 * u >= end) break;                      // wavefront-uniform
+      if (le[u] >= 0) {
+        const uint32_t t = (uint32_t)(beg + 64 * u + lane) / (uint32_t)k;
+        const uint32_t bit = 1u << (t & 31);
+        rep |= (atomicOr(&bits[(t >> 5) * 64 + le[u]], bit) & bit) != 0u;
+      }
+    }
+    if (rep) *repeat = 1;
+    __syncthreads();
+    if (*repeat == 0) {                                    // workgroup-uniform
+      if (wv == 0) {                                       // lane e: row e of the bit matrix
+        int run = 0;
+        for (int w0 = 0; w0 < words; w0 += 8) {
+          uint32_t v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = bits[min(w0 + j, words - 1) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (w0 + j < words) {
+              pre[(w0 + j) * 64 + lane] = run;
+              run += __popc(v[j]);
+            }
+        }
+        const int incl = wave_incl_scan(run);             // lanes >= e_local have run = 0
+        goff[lane] = incl - run;
+        if (lane < e_local) group_offsets[lane] = incl - run;
+        if (lane == 63) group_offsets[e_local] = incl;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kSmallSteps; ++u) {
+        if (beg + 64 * u >= end) break;                    // wavefront-uniform
+        const int p = beg + 64 * u + lane;
+        int row = -1;
+        if (le[u] >= 0) {
+          const uint32_t t = (uint32_t)p / (uint32_t)k;
+          const int cell = (int)(t >> 5) * 64 + le[u];
+          row = goff[le[u]] + pre[cell] + __popc(bits[cell] & ((1u << (t & 31)) - 1u));
+          sorted_pairs[row] = p;
+        }
+        if (p < end) pair_pos[p] = row;
+      }
+      return;
+    }
+  }
+
   int32_t* mine = lds + wv * e_local;
 #pragma unroll
   for (int u = 0; u < kSmallSteps; ++u) {
@@ -261,12 +338,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_perm_small(const int32_t* 
     int total = 0;
     if (e < e_local)
       for (int w = 0; w < kSmallWaves; ++w) total += lds[w * e_local + e];
-    int incl = total;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
+    const int incl = wave_incl_scan(total);
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
     int wave_base = 0, block_total = 0;
@@ -322,8 +394,9 @@ hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_
   while ((1 << nbits) < e_local) ++nbits;
   if (P <= kSmallPairs) {
     const int span = ((P + kSmallWaves - 1) / kSmallWaves + 63) / 64 * 64;
-    const size_t lds = sizeof(int32_t) * ((size_t)kSmallWaves * e_local + kSmallWaves);
-    k_perm_small<<<dim3(1), dim3(64 * kSmallWaves), lds, s>>>(blob, P, e_first, e_local, nbits, span,
+    const int words = (e_local <= kBitsMaxExperts && T <= 32 * kBitsMaxWords) ? (T + 31) / 32 : 0;
+    const size_t lds = sizeof(int32_t) * ((size_t)kSmallWaves * e_local + kSmallWaves + 2 * 64 * (size_t)words + 65);
+    k_perm_small<<<dim3(1), dim3(64 * kSmallWaves), lds, s>>>(blob, P, k, e_first, e_local, nbits, span, words,
                                                               sorted_pairs, group_offsets, pair_pos);
     return hipGetLastError();
   }

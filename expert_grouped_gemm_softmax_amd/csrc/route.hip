@@ -6,10 +6,11 @@
 // all-gather: ids and weight bits stacked on a new leading axis in one int32 array).
 //
 // One 64-lane wavefront owns one token: lane l holds logits l, l+64, l+128, ... in registers as
-// 64-bit selection keys (logit order, then lower expert id), sorted once per lane; each of the k
-// rounds is a 6-step DPP max of the lane heads (4 steps inside each 16-lane row, 2 row broadcasts)
-// read from lane 63 with v_readlane.  The weights need no E-term reduction: slot j's
-// weight only involves the k selected logits.
+// order-mapped value bits with their ids, sorted once per lane; each of the k rounds is a 6-step
+// DPP max of the lane heads' value bits (4 steps inside each 16-lane row, 2 row broadcasts) read
+// from lane 63, a ballot of the heads holding that value, and (only when several do) a second
+// max over their ids.  The weights need no E-term reduction: slot j's weight only involves the
+// k selected logits.
 #include "common.h"
 
 namespace moe {
@@ -42,39 +43,41 @@ __device__ __forceinline__ float exp_neg(float d) {
   return p * two_n;                                        // exact: the product stays normal
 }
 
-// Selection key of (logit v, expert id): larger key = selected first.  High word: the fp32 bits of
-// v mapped to an unsigned order (-0 folded onto +0); low word: ~id, so equal logits go to the lower
-// id.  Key 0 marks an empty slot (every finite logit maps above it).
-__device__ __forceinline__ uint64_t route_key(float v, int id) {
+// Selection order of (logit v, expert id): larger value first, then lower id.  A logit is held as
+// its fp32 bits mapped to an unsigned order (-0 folded onto +0) and its id as ~id, so "selected
+// first" is the larger (bits, ~id) pair.  Bits 0 mark an empty slot (every finite logit maps
+// above it).
+__device__ __forceinline__ uint32_t order_bits(float v) {
   uint32_t b = __float_as_uint(v);
   if (b == 0x80000000u) b = 0u;                            // -0 equals +0
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)~id;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t b = (uint32_t)(key >> 32);
+__device__ __forceinline__ float order_value(uint32_t b) {
   return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
 }
-__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
 
 // DPP controls (gfx9 encoding): quad permutations, reverse within 8 lanes, reverse within 16,
 // and the wave64 row broadcasts of lane 15 (to the next row) and lane 31 (to rows 2 and 3).
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
-// max(k, k of the DPP source lane); lanes outside ROW_MASK keep k (their DPP result is the key 0).
+// max(x, x of the DPP source lane); lanes outside ROW_MASK keep x (their DPP result is 0).
 template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROW_MASK, 0xf, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROW_MASK, 0xf, false);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  return o > k ? o : k;
+__device__ __forceinline__ uint32_t dpp_max(uint32_t x) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+  return o > x ? o : x;
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t k, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, l);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
+// Largest x over the wavefront (all 64 lanes active), wave-uniform: the maximum of each 16-lane
+// row in four steps, then rows 1 and 3 take rows 0 and 2, row 3 takes row 1; lane 63 holds it.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = dpp_max<kQuadXor1>(x);
+  x = dpp_max<kQuadXor2>(x);
+  x = dpp_max<kRowHalfMirror>(x);
+  x = dpp_max<kRowMirror>(x);
+  x = dpp_max<kRowBcast15, 0xa>(x);
+  x = dpp_max<kRowBcast31, 0xc>(x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // ids / w / blob: outputs (a NULL pointer is not written; ids and w are NULL together).
@@ -87,45 +90,60 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                     // uniform per wave
   const float* row = logits + (size_t)t * E;
-  // Lane l owns experts l, l+64, ...; its keys are sorted once (descending), so each round only
-  // compares the heads of the 64 lists and the winning lane drops its head.
-  uint64_t key[PER_LANE];
+  // Lane l owns experts l, l+64, ...: value bits vb and ~id ib, sorted once (descending value;
+  // insertion sort with strict comparisons is stable, so equal values keep ascending id), so each
+  // round only compares the heads of the 64 lists and the winning lane drops its head.  Loads are
+  // unconditional (clamped index): none waits behind a branch.
+  uint32_t vb[PER_LANE], ib[PER_LANE];
+  float x[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) x[i] = __builtin_nontemporal_load(row + min(lane + 64 * i, E - 1));
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? route_key(__builtin_nontemporal_load(row + e), e) : 0ull;
+    vb[i] = (e < E) ? order_bits(x[i]) : 0u;
+    ib[i] = ~(uint32_t)e;
   }
 #pragma unroll
-  for (int i = 1; i < PER_LANE; ++i)                      // insertion sort, fully unrolled
+  for (int i = 1; i < PER_LANE; ++i)
 #pragma unroll
     for (int j = i; j > 0; --j) {
-      const uint64_t a = key[j - 1], b2 = key[j];
-      key[j - 1] = a > b2 ? a : b2;
-      key[j] = a > b2 ? b2 : a;
+      const bool sw = vb[j] > vb[j - 1];
+      const uint32_t v0 = vb[j - 1], v1 = vb[j], i0 = ib[j - 1], i1 = ib[j];
+      vb[j - 1] = sw ? v1 : v0;
+      vb[j] = sw ? v0 : v1;
+      ib[j - 1] = sw ? i1 : i0;
+      ib[j] = sw ? i0 : i1;
     }
-  uint64_t sel = 0;                                       // slot `lane` (lanes < k)
+  uint32_t sel_v = 0, sel_i = 0;                          // slot `lane` (lanes < k)
   for (int j = 0; j < k; ++j) {
-    uint64_t m = key[0];
-    // largest head of each 16-lane row, in every lane of that row
-    m = dpp_max<kQuadXor1>(m);
-    m = dpp_max<kQuadXor2>(m);
-    m = dpp_max<kRowHalfMirror>(m);
-    m = dpp_max<kRowMirror>(m);
-    // rows 1 and 3 take the max with rows 0 and 2, then row 3 with row 1: lane 63 holds the largest
-    m = dpp_max<kRowBcast15, 0xa>(m);
-    m = dpp_max<kRowBcast31, 0xc>(m);
-    const uint64_t best = readlane64(m, 63);          // wave-uniform
-    if (key[0] == best) {                                 // the winner's list advances
-#pragma unroll
-      for (int i = 0; i + 1 < PER_LANE; ++i) key[i] = key[i + 1];
-      key[PER_LANE - 1] = 0ull;
+    const uint32_t best_v = wave_max(vb[0]);
+    const uint64_t tied = __ballot(vb[0] == best_v);
+    int win;
+    if (__popcll(tied) == 1) {
+      win = __ffsll((unsigned long long)tied) - 1;
+    } else {                                              // equal values at several heads: lowest id
+      const uint32_t best_i = wave_max(vb[0] == best_v ? ib[0] : 0u);
+      win = __ffsll((unsigned long long)__ballot(vb[0] == best_v && ib[0] == best_i)) - 1;
     }
-    if (lane == j) sel = best;
+    const uint32_t best_i = (uint32_t)__builtin_amdgcn_readlane((int)ib[0], win);
+    if (lane == win) {                                     // the winner's list advances
+#pragma unroll
+      for (int i = 0; i + 1 < PER_LANE; ++i) {
+        vb[i] = vb[i + 1];
+        ib[i] = ib[i + 1];
+      }
+      vb[PER_LANE - 1] = 0u;
+    }
+    if (lane == j) {
+      sel_v = best_v;
+      sel_i = best_i;
+    }
   }
-  const float sel_v = key_value(sel);
-  const int sel_id = key_id(sel);
-  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
-  const float e = (lane < k) ? exp_neg(sel_v - m) : 0.0f;
+  const float sel_x = order_value(sel_v);
+  const int sel_id = (int)~sel_i;
+  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_x), 0));
+  const float e = (lane < k) ? exp_neg(sel_x - m) : 0.0f;
   float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 0));
   for (int j = 1; j < k; ++j) s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), j));
   if (lane < k) {

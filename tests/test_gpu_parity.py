@@ -163,6 +163,37 @@ def test_fp32_gemm_reads_both_dense_layouts_identically():
     assert torch.equal(h2[:n].view(torch.int32), b.h[:n].view(torch.int32))
 
 
+def _permute_vs_oracle(ids, e_first, e_local):
+    T, k = ids.shape
+    blob_np = oracle.pack(ids.astype(np.int32), np.full((T, k), 1.0 / k, np.float32))
+    sp, off, pp = ops.permute(torch.from_numpy(blob_np).to(_dev()), e_first, e_local)
+    torch.cuda.synchronize()
+    r_sp, r_off, r_pp = oracle.permute(blob_np, e_first, e_local)
+    assert np.array_equal(_np(off), r_off)
+    assert np.array_equal(_np(sp)[:len(r_sp)], r_sp)
+    assert np.array_equal(_np(pp), r_pp)
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 511, 512, 1500, 2047, 2048])
+def test_permute_distinct_experts_token_counts(T):
+    # every token routes to k distinct experts (as top-k does); token counts around 32-token words
+    rng = np.random.default_rng(T)
+    k, E = 8, 200
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    for e_first, e_local in [(0, 64), (37, 64), (150, 50), (0, 1), (10, 65)]:
+        _permute_vs_oracle(ids, e_first, e_local)
+
+
+@pytest.mark.parametrize("T,k", [(300, 6), (2000, 8), (5, 64), (3000, 6)])
+def test_permute_repeated_experts_within_a_token(T, k):
+    # the permutation is defined for any ids, including a token that names one expert twice
+    rng = np.random.default_rng(T * k)
+    ids = rng.integers(0, 40, size=(T, k))
+    ids[0, :] = 7                                               # one token, all slots one expert
+    for e_first, e_local in [(4, 24), (0, 40), (0, 100)]:
+        _permute_vs_oracle(ids, e_first, e_local)
+
+
 def test_permute_with_no_local_pair():
     T, k = 50, 4
     ids = np.stack([np.arange(100, 104)] * T).astype(np.int32)
