@@ -618,22 +618,31 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
     if constexpr (NM > 0) {
       const u16* sA = smem + (kc & 1) * C::STAGE;
       const u16* sB = sA + C::A_ELEMS;
+      // Every operand of the chunk is read before its MFMAs: LDS reads return in order, so each
+      // MFMA waits only for its own operands and the later reads overlap the earlier MFMAs.
+      constexpr int KS = C::KC / 32;
+      bf16x8 av[KS][NM], bv[KS][C::NW][C::NTL];
 #pragma unroll
-      for (int ks = 0; ks < C::KC; ks += 32) {
-        bf16x8 av[NM];
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int i = 0; i < NM; ++i)
-          av[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off_rows(arow, (ks + kofs) >> 3) + i * 16 * C::WM * 64);
+          av[ks][i] = *reinterpret_cast<const bf16x8*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
 #pragma unroll
         for (int m = 0; m < C::NW; ++m)
 #pragma unroll
-          for (int j = 0; j < C::NTL; ++j) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64);
+          for (int j = 0; j < C::NTL; ++j)
+            bv[ks][m][j] = *reinterpret_cast<const bf16x8*>(sB + lds_off_rows(bcol, (ks * 32 + kofs) >> 3) + (m * C::BN + j * 16) * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);           // keep the reads ahead of the MFMAs
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+          for (int j = 0; j < C::NTL; ++j)
 #pragma unroll
             for (int i = 0; i < NM; ++i)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
-          }
-      }
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks][i], bv[ks][m][j], acc[m][i][j], 0, 0, 0);
     }
   }
   __syncthreads();
