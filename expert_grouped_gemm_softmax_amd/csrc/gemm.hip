@@ -302,8 +302,8 @@ __device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>&
 // MFMAs of one LDS chunk for the NM live 16-row tiles of this wave (tile i covers rows
 // arow0 - lane%16 + 16 * WM * i: the 16-row tiles of a workgroup tile are dealt to its WM wave
 // rows in turn, which balances partially filled tiles).
-template <class C, int NM>
-__device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW][NM > 0 ? NM : 1][C::NTL],
+template <class C, int NM, int NA = (NM > 0 ? NM : 1)>
+__device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW][NA][C::NTL],
                                               int arow, int bcol, int kofs) {
   if constexpr (NM > 0) {
     const u16* sA = buf;
@@ -527,6 +527,152 @@ void k_gemm_bf16(GemmParams p) {
       }
     }
     tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// One-buffer tiles, dense weights, activation rows in sorted order (no gather): chunk loads run
+// across tile boundaries.  A workgroup that owns several tiles (the down projection of a
+// decode-shaped batch: K = I is short, N = H wide) loads the first two chunks of its next tile
+// behind the last two chunks of the current one, so they are in flight during that tile's last
+// MFMAs and its epilogue.  Same tiles, LDS layout, operand reads and epilogue as k_gemm_bf16.
+// ---------------------------------------------------------------------------------------------
+// Loading context of one tile; valid = false gives descriptors of range 0 (every load returns
+// zeros without a memory request).
+template <class C>
+__device__ __forceinline__ TileCtx<C> stream_ctx(const GemmParams& p, const TileCoord& tc, bool valid, uint32_t a_bytes,
+                                                 uint32_t w_bytes, int tid, int lane, int wave) {
+  TileCtx<C> t;
+  t.ar = make_rsrc(p.a, valid ? a_bytes : 0u);
+  t.nK = p.K / C::KC;
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int c = (tid + C::NT * i) % C::A_CHUNKS;
+    const int r = c / (C::KC / 8), kc8 = c % (C::KC / 8);
+    const int src = min(tc.row0 + min(r, tc.rows - 1), p.a_rows - 1);
+    t.a_off[i] = r < tc.rows ? (uint32_t)(((size_t)src * p.K + kc8 * 8) * 2) : 0x80000000u;
+  }
+  t.a_lds = lds_off_rows((tid % C::A_CHUNKS) / (C::KC / 8), tid % (C::KC / 8));
+#pragma unroll
+  for (int m = 0; m < C::NW; ++m)
+    t.wr[m] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)tc.e * w_bytes, valid ? w_bytes : 0u);
+  t.row_bytes = p.K * 2;
+  t.b_voff = (uint32_t)((lane >> 3) * t.row_bytes + (lane & 7) * 16);
+  t.b_soff = (uint32_t)((tc.n0 + wave * 8) * t.row_bytes);
+  t.b_lds = lds_off_rows(wave * 8 + (lane >> 3), lane & 7);
+  return t;
+}
+
+// Epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile (SwiGLU of the gate
+// and up values for gate/up tiles); rows past the tile's last row are not written.
+template <class C, typename OutT, int NM, int NA = (NM > 0 ? NM : 1)>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[C::NW][NA][C::NTL], OutT* O, int N, int lane,
+                                           int wrow0, int wcol0, int row0, int rows, int n0) {
+#pragma unroll
+  for (int i = 0; i < NM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wrow0 + i * 16 * C::WM + (lane >> 4) * 4 + r;
+        const int col = wcol0 + j * 16 + (lane & 15);
+        if (row < rows) {
+          float v;
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
+          else v = acc[0][i][j][r];
+          OutT* dst = O + (size_t)(row0 + row) * N + n0 + col;
+          if constexpr (sizeof(OutT) == 4) *dst = v;
+          else *dst = f32_to_bf16(v);
+        }
+      }
+}
+
+// MFMAs of one LDS chunk, or the epilogue, for nm (wave-uniform) live 16-row tiles on accumulators
+// sized for the largest count: only a branch picks the instance, so the registers of the chunks
+// in flight stay where they are.
+template <class C, int NM = 1>
+__device__ __forceinline__ void compute_chunk_nm(int nm, const u16* buf, f32x4 (&acc)[C::NW][C::MT][C::NTL],
+                                                 int arow, int bcol, int kofs) {
+  if constexpr (NM <= C::MT) {
+    if (nm == NM) compute_chunk<C, NM, C::MT>(buf, acc, arow, bcol, kofs);
+    else compute_chunk_nm<C, NM + 1>(nm, buf, acc, arow, bcol, kofs);
+  }
+}
+template <class C, typename OutT, int NM = 1>
+__device__ __forceinline__ void store_tile_nm(int nm, const f32x4 (&acc)[C::NW][C::MT][C::NTL], OutT* O, int N,
+                                              int lane, int wrow0, int wcol0, const TileCoord& tc) {
+  if constexpr (NM <= C::MT) {
+    if (nm == NM) store_tile<C, OutT, NM, C::MT>(acc, O, N, lane, wrow0, wcol0, tc.row0, tc.rows, tc.n0);
+    else store_tile_nm<C, OutT, NM + 1>(nm, acc, O, N, lane, wrow0, wcol0, tc);
+  }
+}
+
+template <class C, typename OutT>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD)))
+void k_gemm_stream(GemmParams p) {
+  static_assert(C::STAGES == 1 && !C::Q4, "one LDS buffer, dense weights");
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  extern __shared__ __attribute__((aligned(16))) u16 smem[];
+  u16* buf = smem;
+  int* s_tstart = reinterpret_cast<int*>(smem + C::STAGE);
+  int* s_goff = s_tstart + (p.n_groups + 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = p.N / BN;
+  const int wrow0 = wm * 16, wcol0 = wn * (BN / WN);
+  build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
+  __syncthreads();
+  const TileIter it = tile_range(s_tstart[p.n_groups]);
+  if (it.next >= it.end) return;
+  OutT* O = static_cast<OutT*>(p.out);
+  // the host checks a_rows * K * 2 < 2^31 and K * N * 2 < 2^32
+  const uint32_t a_bytes = (uint32_t)((size_t)p.a_rows * p.K * 2), w_bytes = (uint32_t)((size_t)p.K * p.N * 2);
+  const int arow = wrow0 + (lane & 15), bcol = wcol0 + (lane & 15), kofs = (lane >> 4) * 8;
+
+  TileCoord tc = tile_coord(s_tstart, s_goff, p.n_groups, it.next, BM, BN, tiles_n);
+  TileCtx<C> t = stream_ctx<C>(p, tc, true, a_bytes, w_bytes, tid, lane, wave);
+  Chunk<C> c0, c1;
+  load_chunk(t, 0, c0);
+  load_chunk(t, 1, c1);
+  for (int tile = it.next; tile < it.end; tile += it.step) {
+    const bool more = tile + it.step < it.end;        // after the last tile: loads of range 0
+    const TileCoord tcn = tile_coord(s_tstart, s_goff, p.n_groups, more ? tile + it.step : tile, BM, BN, tiles_n);
+    const TileCtx<C> tn = stream_ctx<C>(p, tcn, more, a_bytes, w_bytes, tid, lane, wave);
+    const int nm = min(C::MT, max(0, ((tc.rows + 15) / 16 - wm + WM - 1) / WM));   // live 16-row tiles
+    f32x4 acc[C::NW][C::MT][C::NTL];
+#pragma unroll
+    for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+      for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the chunk count is even: chunks kc and kc + 1 sit in c0 and c1
+    for (int kc = 0; kc + 2 < t.nK; kc += 2) {
+      store_chunk(t, c0, buf);
+      __syncthreads();
+      compute_chunk_nm<C>(nm, buf, acc, arow, bcol, kofs);
+      load_chunk(t, kc + 2, c0);
+      __syncthreads();
+      store_chunk(t, c1, buf);
+      __syncthreads();
+      compute_chunk_nm<C>(nm, buf, acc, arow, bcol, kofs);
+      load_chunk(t, kc + 3, c1);
+      __syncthreads();
+    }
+    store_chunk(t, c0, buf);
+    __syncthreads();
+    compute_chunk_nm<C>(nm, buf, acc, arow, bcol, kofs);
+    load_chunk(tn, 0, c0);
+    __syncthreads();
+    store_chunk(t, c1, buf);
+    __syncthreads();
+    compute_chunk_nm<C>(nm, buf, acc, arow, bcol, kofs);
+    load_chunk(tn, 1, c1);
+    __syncthreads();                               // LDS is refilled by the next tile
+    store_tile_nm<C, OutT>(nm, acc, O, p.N, lane, wrow0, wcol0, tc);
+    tc = tcn;
+    t = tn;
   }
 }
 
@@ -846,6 +992,12 @@ hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
+  if constexpr (C::STAGES == 1 && !C::Q4) {
+    if (p.row_index == nullptr && (p.K / C::KC) % 2 == 0) {
+      k_gemm_stream<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
+      return hipGetLastError();
+    }
+  }
   k_gemm_bf16<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
   return hipGetLastError();
 }
