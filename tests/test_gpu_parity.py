@@ -218,6 +218,10 @@ MID = {
                              wfmt="int4", group_size=128),
     "int4_channel": W.MoEConfig("mid", T=150, H=256, E=16, k=3, I=256, e_first=2, e_local=8,
                                     wfmt="int4", group_size=256),
+    # decode-shaped tiles with about 40 rows per expert: two 32-row tiles per expert, so the down
+    # projection has four tiles per workgroup and its loads run across three tile boundaries
+    "bf16_many_tiles_per_workgroup": W.MoEConfig("mid", T=320, H=4096, E=64, k=8, I=256, e_first=0,
+                                                 e_local=64),
     "f32": W.MoEConfig("mid", T=130, H=256, E=12, k=3, I=192, e_first=1, e_local=9, act="f32"),
     "f32_shared": W.MoEConfig("mid", T=70, H=128, E=8, k=2, I=64, e_first=0, e_local=8, act="f32",
                               shared_I=128),
