@@ -122,6 +122,57 @@ def cpu_baseline(cfg, inp, budget_s: float):
                       f"{pairs} local pairs in {secs:.1f} s on {threads} host threads"}
 
 
+def attainable_peaks():
+    """Measured ceilings on this GPU, next to the published peaks: a bf16 MFMA loop that touches no
+    memory and a streaming read of 2 GiB (well past the 256 MB last-level cache), each the best
+    of a few launches.  None if the calibration library is not built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "expert_grouped_gemm_softmax_amd", "libmoe_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.moe_calib_mfma_flops.restype = ctypes.c_double
+    lib.moe_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+
+    def best(launch, reps=5):
+        launch()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    blocks, iters = cus * 4, 20000
+    t = best(lambda: lib.moe_calib_mfma(blocks, iters, ctypes.c_void_p(sink.data_ptr()), sp))
+    mfma = lib.moe_calib_mfma_flops(blocks, iters) / t / 1e12
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gbs = 0.0
+    for wg_per_cu in (2, 4, 8):
+        blk = cus * wg_per_cu
+        if nbytes % (blk * 256 * 8 * 16):
+            continue
+        t = best(lambda: lib.moe_calib_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blk,
+                                            ctypes.c_void_p(sink.data_ptr()), sp))
+        gbs = max(gbs, nbytes / t / 1e9)
+    del buf
+    torch.cuda.synchronize()
+    return {"hbm_read_gbs": round(gbs, 1), "mfma_bf16_tflops": round(mfma, 1),
+            "how": "best of 5 launches: 2 GiB streaming read (16-byte nontemporal loads, 8 in flight per "
+                   "lane); bf16 16x16x32 MFMA loop on registers, 8 independent accumulators per wave"}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -253,6 +304,13 @@ def main():
         "down_roofline": roofline(cfg, dflops, dbytes, dn_us * 1e-6),
         "gemm_pair_roofline": roofline(cfg, layer_flops, layer_bytes, (gu_us + dn_us) * 1e-6),
     }
+    att = attainable_peaks()
+    out["attainable"] = att
+    if att:
+        if roof["unit"] == "GB/s":
+            roof["frac_of_attainable"] = round(roof["achieved"] / att["hbm_read_gbs"], 4)
+        elif roof["bound"] == "mfma":
+            roof["frac_of_attainable"] = round(roof["achieved"] / att["mfma_bf16_tflops"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -156,3 +156,25 @@ def test_prepare_dense_weights_validation(L):
     assert L.moe_prepare_dense_weights(F, 65536, 64, 64, 1, F, None) == INV
     assert L.moe_prepare_dense_weights(F, 1, (1 << 22) + 1, 64, 1, F, None) == INV
     assert L.moe_prepare_dense_weights(F, 1024, 1 << 15, 1 << 15, 1, F, None) == INV   # 2^40 elements
+
+
+def test_calibration_library_exports_and_rejects_bad_sizes():
+    """The measured-ceiling microkernels used by bench.py (a separate library): symbols, the flop
+    count of the MFMA loop, and argument checks that return before any HIP call."""
+    from expert_grouped_gemm_softmax_amd import build as hip_build
+    if not os.path.exists(hip_build.CALIB_PATH):
+        pytest.fail("libmoe_calib.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(hip_build.CALIB_PATH)
+    lib.moe_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.moe_calib_mfma_flops.restype = ctypes.c_double
+    assert lib.moe_calib_mfma_flops(2, 3) == 2 * 4 * 3 * 8 * 16 * 16 * 32 * 2
+    lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    HIP_INVALID = 1                                   # hipErrorInvalidValue
+    assert lib.moe_calib_mfma(0, 10, FAKE, None) == HIP_INVALID
+    assert lib.moe_calib_mfma(4, 0, FAKE, None) == HIP_INVALID
+    assert lib.moe_calib_mfma(4, 10, None, None) == HIP_INVALID
+    unit = 8 * 256 * 8 * 16
+    assert lib.moe_calib_read(None, unit, 8, FAKE, None) == HIP_INVALID
+    assert lib.moe_calib_read(FAKE, unit + 16, 8, FAKE, None) == HIP_INVALID
+    assert lib.moe_calib_read(FAKE, unit, 8, None, None) == HIP_INVALID
