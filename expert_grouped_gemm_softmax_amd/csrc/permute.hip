@@ -4,8 +4,10 @@
 // (option B): each device keeps only the token-expert pairs routed to its own experts.  They are
 // grouped by expert with a stable counting sort: histogram, exclusive prefix scan, scatter.
 //
-// Up to kSmallPairs pairs: one launch, one workgroup of 16 wavefronts (k_perm_small): count per
-// wavefront in LDS, scan over experts, recount and write.  Larger inputs: two launches over chunks
+// Up to kSmallPairs pairs: one launch, one workgroup of 16 wavefronts (k_perm_small).  With at
+// most 64 local experts and 2048 tokens it ranks pairs with an LDS bit per (expert, token) (see
+// the kernel); otherwise it counts per wavefront in LDS, scans over experts, recounts and writes.
+// Larger inputs: two launches over chunks
 // of kChunk consecutive pairs (one workgroup of 4 wavefronts per chunk, 128 pairs per wavefront):
 //   k_perm_count    per-chunk histogram of local expert ids -> workspace counts[chunk][e];
 //   k_perm_scatter  every workgroup sums the counts of the chunks before it (its row base per
@@ -14,7 +16,8 @@
 // Inside a 64-pair step, lanes carrying the same local expert are found with one ballot per bit
 // of the local id (a match-any built from ballots); the lowest such lane updates the wavefront's
 // LDS counter for that expert.  Stable order = (chunk, wavefront, step, lane) = ascending pair
-// index, with no atomics, so the result is deterministic.
+// index.  The only atomics are the token-bit path's OR into LDS, whose result does not depend on
+// their order, so every output is deterministic.
 #include "common.h"
 
 namespace moe {
