@@ -244,6 +244,26 @@ def test_layer_mid_size_every_token(name, variant):
         assert np.all(_np(y)[counts == 0] == 0.0)
 
 
+def test_layer_on_two_side_streams_matches_the_default_stream():
+    # every kernel goes on the caller's stream, and calls on different streams (separate buffers)
+    # may run at the same time: both results equal the default-stream result bit for bit
+    cfg = MID["bf16_ragged"]
+    inp = W.make_inputs(cfg)
+    x, logits, wts = upload(inp, cfg, _dev())
+    y0 = MoELayer.from_config(cfg, wts).forward(x, logits).clone()
+    torch.cuda.synchronize()
+    layers = [MoELayer.from_config(cfg, wts) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]          # default priority
+    outs = []
+    for layer, s in zip(layers, streams):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            outs.append(layer.forward(x, logits, stream=s))
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y.view(torch.int32), y0.view(torch.int32))
+
+
 def test_layer_bf16_output_is_rounded_fp32_output_and_deterministic():
     """The bf16 layer output is the round-to-nearest-even of the fp32 output (the combine
     accumulates in fp32 either way), and repeated calls are bitwise identical."""
