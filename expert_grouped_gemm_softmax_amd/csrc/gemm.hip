@@ -872,6 +872,230 @@ void k_gemm_dma(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The same tiles with three weight buffers: weight chunks are copied two chunks ahead (activation
+// chunks, mostly L2 hits, one ahead).  Two activation and three weight buffers of a 256-row tile
+// take all 160 KB of LDS, so the tile table lives in registers instead (one lane per expert, up
+// to 64 experts): every wave scans the group sizes itself and finds a tile's expert with a ballot.
+// ---------------------------------------------------------------------------------------------
+struct RegTable {
+  int lo, hi, tstart;                              // lane e: rows [lo, hi) of group e, its first tile
+  int total;
+};
+
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Same tile numbering as build_tile_table (n_groups <= 64).
+__device__ __forceinline__ RegTable reg_tile_table(const GemmParams& p, int BM, int tiles_n, int lane) {
+  RegTable r;
+  int tiles = 0;
+  r.lo = 0;
+  r.hi = 0;
+  if (lane < p.n_groups) {
+    r.lo = min(max(p.group_offsets[lane], 0), p.rows_cap);
+    r.hi = min(max(p.group_offsets[lane + 1], r.lo), p.rows_cap);
+    tiles = ((r.hi - r.lo + BM - 1) / BM) * tiles_n;
+  }
+  const int incl = wave_scan_incl(tiles);
+  r.tstart = incl - tiles;
+  r.total = __builtin_amdgcn_readlane(incl, 63);
+  return r;
+}
+
+__device__ __forceinline__ TileCoord reg_tile_coord(const RegTable& r, int n_groups, int lane, int tile, int BM, int BN,
+                                                    int tiles_n) {
+  constexpr int kGroupM = 4;
+  // the expert is the last group whose first tile is <= tile (empty groups before it start at or
+  // before it, those after it start after it)
+  const uint64_t m = __ballot(lane < n_groups && r.tstart <= tile);
+  const int e = 63 - __builtin_clzll(m);
+  const int g0 = __builtin_amdgcn_readlane(r.lo, e), g1 = __builtin_amdgcn_readlane(r.hi, e);
+  const int local = tile - __builtin_amdgcn_readlane(r.tstart, e);
+  const int mtiles = (g1 - g0 + BM - 1) / BM;
+  const int grp = local / (kGroupM * tiles_n), in_grp = local % (kGroupM * tiles_n);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int mt = grp * kGroupM + in_grp % gm, nt = in_grp / gm;
+  const int row0 = g0 + mt * BM;
+  return {e, row0, min(BM, g1 - row0), nt * BN};
+}
+
+// Wait until at most N vector memory instructions of this wave are outstanding (they complete in
+// issue order, so every older one has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// LDS: activation buffers [2][A_ELEMS], then weight buffers [3][B_ELEMS].
+template <class C>
+__device__ __forceinline__ void dma3_a(const DmaCtx<C>& t, int kc, int buf) {
+  const uint32_t st = t.lds + (uint32_t)buf * C::A_ELEMS * 2;
+#pragma unroll
+  for (int j = 0; j < C::A_INST; ++j)
+    lds_dma16(t.ar, t.a_voff[j], (uint32_t)kc * 128, st + 8 * (t.wave + C::NWAVES * j) * 128);
+}
+template <class C>
+__device__ __forceinline__ void dma3_b(const DmaCtx<C>& t, int kc, int buf) {
+  const uint32_t st = t.lds + (uint32_t)(2 * C::A_ELEMS + buf * C::B_ELEMS) * 2;
+#pragma unroll
+  for (int j = 0; j < C::B_INST; ++j) {
+    __amdgpu_buffer_rsrc_t w = t.wr[0];
+    if constexpr (C::NW == 2) w = t.b_m[j] ? t.wr[1] : t.wr[0];
+    lds_dma16(w, t.b_voff, t.b_soff[j] + (uint32_t)kc * 128, st + 8 * (t.wave + C::NWAVES * j) * 128);
+  }
+}
+
+template <class C, typename OutT, int NM>
+__device__ __forceinline__ void dma3_tile(const DmaCtx<C>& t, u16* smem, OutT* O, int N, int lane, int wrow0, int wcol0,
+                                          const TileCoord& tc) {
+  f32x4 acc[C::NW][NM > 0 ? NM : 1][C::NTL];
+#pragma unroll
+  for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+    for (int i = 0; i < (NM > 0 ? NM : 1); ++i)
+#pragma unroll
+      for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int arow = wrow0 + (lane & 15), bcol = wcol0 + (lane & 15), kofs = (lane >> 4) * 8;
+  const int nK = t.nK;
+  // Issue order: A(0), B(0), B(1); iteration kc then issues A(kc+1) and B(kc+2).  At the top of
+  // iteration kc only weight chunk kc+1 may still be outstanding after A(kc) and B(kc).
+  wait_vmcnt0();                                   // nothing of the previous tile is in flight
+  dma3_a(t, 0, 0);
+  dma3_b(t, 0, 0);
+  if (nK > 1) dma3_b(t, 1, 1);
+  int sb = 0;                                      // weight buffer of chunk kc
+  for (int kc = 0; kc < nK; ++kc) {
+    if (kc + 1 < nK) wait_vmcnt_n<C::B_INST>();
+    else wait_vmcnt0();
+    __syncthreads();                               // everyone's chunk kc; buffers of chunk kc-1 free
+    if (kc + 1 < nK) dma3_a(t, kc + 1, (kc + 1) & 1);
+    if (kc + 2 < nK) dma3_b(t, kc + 2, sb == 0 ? 2 : sb - 1);
+    if constexpr (NM > 0) {
+      const u16* sA = smem + (kc & 1) * C::A_ELEMS;
+      const u16* sB = smem + 2 * C::A_ELEMS + sb * C::B_ELEMS;
+      constexpr int KS = C::KC / 32;
+      bf16x8 av[KS][NM], bv[KS][C::NW][C::NTL];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i)
+          av[ks][i] = *reinterpret_cast<const bf16x8*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
+#pragma unroll
+        for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+          for (int j = 0; j < C::NTL; ++j)
+            bv[ks][m][j] = *reinterpret_cast<const bf16x8*>(sB + lds_off_rows(bcol, (ks * 32 + kofs) >> 3) + (m * C::BN + j * 16) * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);           // keep the reads ahead of the MFMAs
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+          for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+            for (int i = 0; i < NM; ++i)
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks][i], bv[ks][m][j], acc[m][i][j], 0, 0, 0);
+    }
+    sb = sb == 2 ? 0 : sb + 1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wrow0 + i * 16 * C::WM + (lane >> 4) * 4 + r;
+        const int col = wcol0 + j * 16 + (lane & 15);
+        if (row < tc.rows) {
+          float v;
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
+          else v = acc[0][i][j][r];
+          OutT* dst = O + (size_t)(tc.row0 + row) * N + tc.n0 + col;
+          if constexpr (sizeof(OutT) == 4) *dst = v;
+          else *dst = f32_to_bf16(v);
+        }
+      }
+}
+
+template <class C, typename OutT, int NM>
+__device__ __forceinline__ void dma3_dispatch(int nm, const DmaCtx<C>& t, u16* smem, OutT* O, int N, int lane,
+                                              int wrow0, int wcol0, const TileCoord& tc) {
+  if constexpr (NM <= C::MT) {
+    if (nm == NM) dma3_tile<C, OutT, NM>(t, smem, O, N, lane, wrow0, wcol0, tc);
+    else dma3_dispatch<C, OutT, NM + 1>(nm, t, smem, O, N, lane, wrow0, wcol0, tc);
+  }
+}
+
+template <class C, typename OutT>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD)))
+void k_gemm_dma3(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  extern __shared__ __attribute__((aligned(16))) u16 smem_dma3[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = p.N / BN;
+  const int wrow0 = wm * 16, wcol0 = wn * (BN / WN);
+  const RegTable tab = reg_tile_table(p, BM, tiles_n, lane);
+  const TileIter it = tile_range(tab.total);
+  DmaCtx<C> t;
+  t.ar = make_rsrc(p.a, (uint32_t)((size_t)p.a_rows * p.K * 2));
+  t.wave = wave;
+  t.nK = p.K / C::KC;
+  t.lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)smem_dma3);
+  const uint32_t w_bytes = (uint32_t)((size_t)p.K * p.N * 2);
+  const uint32_t row_bytes = (uint32_t)p.K * 2;
+  // lane i fills row i / 8 of an 8-row block at chunk position i % 8; the block starts at a row
+  // 8 * (wave + NWAVES * j), so the row's swizzle (row / 2) mod 8 is (i / 16) ^ 4 * (wave & 1)
+  const int q = (lane & 7) ^ (lane >> 4) ^ (4 * (wave & 1));
+  t.b_voff = (uint32_t)(lane >> 3) * row_bytes + q * 16;
+  OutT* O = static_cast<OutT*>(p.out);
+  for (int tile = it.next; tile < it.end; tile += it.step) {
+    const TileCoord tc = reg_tile_coord(tab, p.n_groups, lane, tile, BM, BN, tiles_n);
+    const int nm = min(C::MT, max(0, ((tc.rows + 15) / 16 - wm + WM - 1) / WM));
+#pragma unroll
+    for (int m = 0; m < C::NW; ++m)
+      t.wr[m] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)tc.e * w_bytes, w_bytes);
+#pragma unroll
+    for (int j = 0; j < C::A_INST; ++j) {
+      const int r = 8 * (wave + C::NWAVES * j) + (lane >> 3);
+      const int rr = tc.row0 + min(r, tc.rows - 1);
+      int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
+      src = min(max(src, 0), p.a_rows - 1);
+      t.a_voff[j] = r < tc.rows ? (uint32_t)(((size_t)src * p.K + q * 8) * 2) : 0x80000000u;
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_INST; ++j) {
+      const int rb = 8 * (wave + C::NWAVES * j);
+      t.b_m[j] = rb / BN;
+      t.b_soff[j] = (uint32_t)(tc.n0 + rb % BN) * row_bytes;
+    }
+    dma3_dispatch<C, OutT, 0>(nm, t, smem_dma3, O, p.N, lane, wrow0, wcol0, tc);
+  }
+}
+
+template <class C, typename OutT>
+hipError_t run_dma3(const GemmParams& p, hipStream_t s) {
+  if (p.N % C::BN != 0 || p.n_groups > 64) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(2 * C::A_ELEMS + 3 * C::B_ELEMS) * 2;
+  if (lds > kLdsPerCu) return hipErrorInvalidValue;
+  const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
+  long long grid = device_cu_count();
+  if (grid > max_tiles) grid = max_tiles;
+  grid = ((grid + 7) / 8) * 8;
+  if (grid < 8) grid = 8;
+  k_gemm_dma3<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
+  return hipGetLastError();
+}
+
 template <class C, typename OutT>
 hipError_t run_dma(const GemmParams& p, hipStream_t s) {
   if (p.N % C::BN != 0) return hipErrorInvalidValue;   // the caller picks a narrower tile
@@ -1082,7 +1306,8 @@ static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, b
   // Tile shapes: rows x columns per tile for gate/up | down, waves, LDS buffers, workgroups per CU.
   //   0 (decode):          32x64   | 32x128,  4 waves (1x4), 1 buffer,  4/CU, two chunks in registers
   //   1 (prefill):         256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU; dense weights: direct
-  //                        global -> LDS loads; int4: one chunk in registers (dequantised on the way)
+  //                        global -> LDS loads (down, up to 64 experts: three weight buffers);
+  //                        int4: one chunk in registers (dequantised on the way)
   //   2 (prefill, narrow): 256x64  | 256x128, 4 waves (4x1), 2 buffers, 1/CU, two chunks in registers
   const bool n256 = p.N % 256 == 0;
   if (gu) {
@@ -1094,10 +1319,15 @@ static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, b
   }
   switch (v) {
     case 0: return run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, s);
-    case 1:
+    case 1: {
       if (!n256) return hipErrorInvalidValue;
       if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s);
+      // three weight buffers (up to 64 experts: the tile table then fits in registers)
+      const hipError_t e = f32out ? run_dma3<DCfg<256, 256, 4, 2, false>, float>(p, s)
+                                  : run_dma3<DCfg<256, 256, 4, 2, false>, u16>(p, s);
+      if (e != hipErrorInvalidValue) return e;
       return f32out ? run_dma<DCfg<256, 256, 4, 2, false>, float>(p, s) : run_dma<DCfg<256, 256, 4, 2, false>, u16>(p, s);
+    }
     default: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, s);
   }
 }

@@ -222,6 +222,8 @@ MID = {
     # projection has four tiles per workgroup and its loads run across three tile boundaries
     "bf16_many_tiles_per_workgroup": W.MoEConfig("mid", T=320, H=4096, E=64, k=8, I=256, e_first=0,
                                                  e_local=64),
+    # more than 64 local experts: the prefill down tiles fall back to the LDS tile table
+    "bf16_80_local_experts": W.MoEConfig("mid", T=160, H=512, E=128, k=8, I=128, e_first=16, e_local=80),
     "f32": W.MoEConfig("mid", T=130, H=256, E=12, k=3, I=192, e_first=1, e_local=9, act="f32"),
     "f32_shared": W.MoEConfig("mid", T=70, H=128, E=8, k=2, I=64, e_first=0, e_local=8, act="f32",
                               shared_I=128),
