@@ -325,3 +325,34 @@ def test_layer_full_workload_sampled(name):
         assert np.all(yn[loc == 0] == 0.0)
     print(name, "n_loc", int(off[-1]), "empty groups", int((np.diff(off) == 0).sum()),
           "max group", int(np.diff(off).max()))
+
+
+# ----------------------------------------------------------------------------------------------
+# The largest activation matrix the library accepts: the down projection's input h (written by
+# the gate/up GEMM) just under 2^31 bytes, so its last rows sit at the top of the kernels' 32-bit
+# byte offsets (both tile families)
+# ----------------------------------------------------------------------------------------------
+MAX_ROWS = W.MoEConfig("max_rows", T=(1 << 31) // (8192 * 2) - 1, H=256, E=8, k=1, I=8192, e_first=0,
+                       e_local=8)
+
+
+@pytest.fixture(scope="module")
+def max_rows_inputs():
+    return W.make_inputs(MAX_ROWS, threads=16)
+
+
+@pytest.mark.parametrize("variant", ["small_m", "large_m"])
+def test_layer_at_the_largest_activation_matrix(max_rows_inputs, variant):
+    cfg, inp = MAX_ROWS, max_rows_inputs
+    layer, b, y = _run(cfg, inp, m_hint=(8 if variant == "small_m" else 0))
+    ids, w, off = _check_routing(b, inp, cfg)
+    n_loc = int(off[-1])
+    assert n_loc == cfg.T and n_loc * cfg.I * 2 < (1 << 31) <= (n_loc + 1) * cfg.I * 2
+    toks, loc = _sample_tokens(cfg, ids)
+    last = int(_np(b.sorted_pairs)[n_loc - 1])         # the pair whose h row is the last one
+    toks = np.unique(np.concatenate([toks, [last // cfg.k]])).astype(np.int32)
+    ref = oracle.layer(inp, cfg, ids, w, tokens=toks, threads=8)
+    yn = y[torch.from_numpy(toks).long().to(y.device)].float().cpu().numpy().astype(np.float64)
+    _check_close(yn, ref, f"max_rows/{variant}")
+    del layer, b, y
+    torch.cuda.empty_cache()
