@@ -109,7 +109,7 @@ def test_routing_bit_exact_random_rank_zipf():
     (1, 4, 1, 0, 4), (3, 7, 7, 2, 5), (77, 64, 1, 0, 64), (129, 1024, 64, 0, 1024),
     (1000, 1024, 10, 512, 512), (257, 513, 33, 100, 413), (4096, 96, 6, 0, 1),
     (65536, 512, 10, 64, 64), (5000, 128, 8, 120, 8), (64, 8, 2, 0, 8),
-    (2048, 64, 8, 0, 64), (2049, 64, 8, 8, 40)])
+    (2048, 64, 8, 0, 64), (2049, 64, 8, 8, 40), (3000, 1024, 16, 0, 1024)])
 def test_routing_bit_exact_edge_shapes(T, E, k, e_first, e_local):
     rng = np.random.default_rng(T + E + k)
     L = (rng.standard_normal((T, E)) * 3).astype(np.float32)
@@ -224,6 +224,9 @@ MID = {
                                                  e_local=64),
     # more than 64 local experts: the prefill down tiles fall back to the LDS tile table
     "bf16_80_local_experts": W.MoEConfig("mid", T=160, H=512, E=128, k=8, I=128, e_first=16, e_local=80),
+    # the most local experts the library accepts: tile tables of 1024 groups (the prefill down
+    # projection falls back to the LDS tile table)
+    "bf16_1024_local_experts": W.MoEConfig("mid", T=600, H=256, E=1024, k=8, I=128, e_first=0, e_local=1024),
     "f32": W.MoEConfig("mid", T=130, H=256, E=12, k=3, I=192, e_first=1, e_local=9, act="f32"),
     "f32_shared": W.MoEConfig("mid", T=70, H=128, E=8, k=2, I=64, e_first=0, e_local=8, act="f32",
                               shared_I=128),
