@@ -28,7 +28,14 @@ int device_cu_count() {
 namespace {
 
 inline bool fits_i32(long long v) { return v >= 0 && v < (long long)INT_MAX; }
-inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Status of one enqueue: the runtime's last-error slot is cleared first, so an error left there by
+// an earlier, unrelated call of the caller is not reported as this call's failure.
+template <class F>
+inline moe_status enqueue(F&& launch) {
+  (void)hipGetLastError();
+  return launch() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -50,7 +57,7 @@ MOE_API moe_status moe_route(const float* logits, int T, int E, int k, int32_t* 
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * E)) return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_w, nullptr, as_stream(stream)));
+  return enqueue([&] { return moe::launch_route(logits, T, E, k, topk_ids, topk_w, nullptr, as_stream(stream)); });
 }
 
 MOE_API moe_status moe_route_packed(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
@@ -58,14 +65,14 @@ MOE_API moe_status moe_route_packed(const float* logits, int T, int E, int k, in
   if (!logits || !blob || (topk_ids == nullptr) != (topk_w == nullptr)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * E) || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_w, blob, as_stream(stream)));
+  return enqueue([&] { return moe::launch_route(logits, T, E, k, topk_ids, topk_w, blob, as_stream(stream)); });
 }
 
 MOE_API moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T, int k,
                                     int32_t* blob, void* stream) {
   if (!topk_ids || !topk_w || !blob) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_pack(topk_ids, topk_w, T, k, blob, as_stream(stream)));
+  return enqueue([&] { return moe::launch_pack(topk_ids, topk_w, T, k, blob, as_stream(stream)); });
 }
 
 MOE_API size_t moe_permute_workspace_bytes(int T, int k, int e_local) {
@@ -83,8 +90,8 @@ MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, i
   const size_t need = moe::permute_workspace_bytes(T, k, e_local);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0))
     return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_permute(blob, T, k, e_first, e_local, sorted_pairs, group_offsets,
-                                      pair_pos, workspace, as_stream(stream)));
+  return enqueue([&] { return moe::launch_permute(blob, T, k, e_first, e_local, sorted_pairs, group_offsets,
+                                      pair_pos, workspace, as_stream(stream)); });
 }
 
 MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
@@ -120,7 +127,7 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   } else if (a->wfmt == MOE_W_DENSE && a->act_dtype == MOE_DT_BF16) {
     return MOE_ERR_UNSUPPORTED;                        // prepare with moe_prepare_dense_weights
   }
-  return from_hip(moe::launch_grouped_gemm(*a, as_stream(stream)));
+  return enqueue([&] { return moe::launch_grouped_gemm(*a, as_stream(stream)); });
 }
 
 MOE_API moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N, int dtype, void* out,
@@ -129,7 +136,7 @@ MOE_API moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N,
   if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (E < 1 || K < 1 || N < 1 || E > 65535 || K > (1 << 22) || (long long)E * K * N >= (1LL << 40))
     return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_prepare(w, E, K, N, dtype, out, as_stream(stream)));
+  return enqueue([&] { return moe::launch_prepare(w, E, K, N, dtype, out, as_stream(stream)); });
 }
 
 MOE_API moe_status moe_combine(const void* expert_out, int expert_rows, int act_dtype, const int32_t* blob,
@@ -140,6 +147,6 @@ MOE_API moe_status moe_combine(const void* expert_out, int expert_rows, int act_
   if (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (expert_rows < 1 || T < 1 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_combine(expert_out, act_dtype, blob, pair_pos, shared_out, T, k, H,
-                                      expert_rows, y, y_dtype, as_stream(stream)));
+  return enqueue([&] { return moe::launch_combine(expert_out, act_dtype, blob, pair_pos, shared_out, T, k, H,
+                                      expert_rows, y, y_dtype, as_stream(stream)); });
 }

@@ -25,8 +25,6 @@
 //    holds the gate and the up value of the same output element).
 //  - Global loads run ahead of the MFMAs through registers (one or two chunks) and one or two
 //    LDS buffers.
-#include <cstdlib>
-
 #include "common.h"
 
 namespace moe {
@@ -1082,11 +1080,12 @@ void k_gemm_dma3(GemmParams p) {
   }
 }
 
+// Launchers.  Each is called only for a shape it handles (the caller checks N against the tile
+// width and the LDS sizes first), so any error they return is a real launch failure.
 template <class C, typename OutT>
 hipError_t run_dma3(const GemmParams& p, hipStream_t s) {
-  if (p.N % C::BN != 0 || p.n_groups > 64) return hipErrorInvalidValue;
+  static_assert((size_t)(2 * C::A_ELEMS + 3 * C::B_ELEMS) * 2 <= kLdsPerCu, "three weight buffers fit in LDS");
   const size_t lds = (size_t)(2 * C::A_ELEMS + 3 * C::B_ELEMS) * 2;
-  if (lds > kLdsPerCu) return hipErrorInvalidValue;
   const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
   long long grid = device_cu_count();
   if (grid > max_tiles) grid = max_tiles;
@@ -1098,9 +1097,8 @@ hipError_t run_dma3(const GemmParams& p, hipStream_t s) {
 
 template <class C, typename OutT>
 hipError_t run_dma(const GemmParams& p, hipStream_t s) {
-  if (p.N % C::BN != 0) return hipErrorInvalidValue;   // the caller picks a narrower tile
+  static_assert(2 * (size_t)C::STAGE * 2 + 2 * 4 * 1025 + 16 <= kLdsPerCu, "two buffers and a 1024-group tile table fit in LDS");
   const size_t lds = C::lds_bytes(p.n_groups);
-  if (lds > kLdsPerCu) return hipErrorInvalidValue;
   const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
   long long grid = device_cu_count();
   if (grid > max_tiles) grid = max_tiles;
@@ -1205,12 +1203,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
 
 template <class C, typename OutT>
 hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
-  if (p.N % C::BN != 0) return hipErrorInvalidValue;   // the caller picks a narrower tile
   const size_t lds = C::lds_bytes(p.n_groups);
   // Upper bound of the tile count: every group adds at most one partial m-tile.
   const long long max_tiles = ((long long)(p.rows_cap + C::BM - 1) / C::BM + p.n_groups) * (p.N / C::BN);
-  const int fit = (int)(kLdsPerCu / lds);              // workgroups that fit in one CU's LDS
-  if (fit < 1) return hipErrorInvalidValue;
+  const int fit = (int)(kLdsPerCu / lds);              // workgroups that fit in one CU's LDS (>= 1)
   if (wgs_per_cu > fit) wgs_per_cu = fit;
   long long grid = (long long)device_cu_count() * wgs_per_cu;
   if (grid > max_tiles) grid = max_tiles;
@@ -1240,12 +1236,17 @@ hipError_t run_f32(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Tile variants.  Decode-shaped calls (few rows per expert) stream weights with 32-row tiles, four
-// workgroups per CU; prefill-shaped calls use 256-row tiles of 8 waves, one workgroup per CU.
-// MOE_GEMM_VARIANT_GU / _DN (tuning sweeps only) force a variant index.
+// Tile variants, chosen on the host from the shape before anything is launched:
+//   0 (decode-shaped, few rows per expert): 32x64 | 32x128 (gate/up | down) tiles, 4 waves (1x4),
+//     1 LDS buffer, two chunks in registers, 4 workgroups per CU (dense down: 2 per CU);
+//   1 (prefill-shaped): 256x128 | 256x256, 8 waves (4x2), 2 LDS buffers, 1 per CU; dense weights go
+//     straight from global memory to LDS (down with up to 64 experts: three weight buffers); int4
+//     words go through one register set and are dequantised on the way;
+//   2 (prefill-shaped, N not a multiple of variant 1's width): 256x64 | 256x128, 4 waves (4x1),
+//     2 LDS buffers, 1 per CU, two chunks in registers.
+// Every variant's LDS (two 256-row buffers and a tile table of up to 1024 groups) fits in 160 KB.
 namespace {
 
-// Whether a tile shape splits evenly over its workgroup (mirrors the static checks of Cfg).
 template <int BM, int BN, int WM, int WN, bool GU>
 constexpr bool cfg_ok() {
   constexpr int NT = 64 * WM * WN, NW = GU ? 2 : 1, A_CHUNKS = BM * 8;
@@ -1256,6 +1257,8 @@ constexpr bool cfg_ok() {
 template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
 hipError_t run_gu(const GemmParams& p, bool q4, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, true>(), "gate/up tile");
+  static_assert(Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>::STAGES * Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>::STAGE * 2 +
+                    2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
   return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>, u16>(p, WGS, s)
             : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS, RS>, u16>(p, WGS, s);
 }
@@ -1263,6 +1266,8 @@ hipError_t run_gu(const GemmParams& p, bool q4, hipStream_t s) {
 template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
 hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, false>(), "down tile");
+  static_assert(Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>::STAGES * Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>::STAGE * 2 +
+                    2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
   if (f32out)
     return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, float>(p, WGS, s)
               : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, float>(p, WGS, s);
@@ -1270,14 +1275,7 @@ hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, hipStream_t s) {
             : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, u16>(p, WGS, s);
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
-
 }  // namespace
-
-static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, hipStream_t s);
 
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   GemmParams p;
@@ -1293,47 +1291,24 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   }
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
   const bool f32out = a.out_dtype == MOE_DT_F32;
+  // The ABI guarantees N % 64 == 0 (gate/up) and N % 128 == 0 (down): variants 0 and 2 always fit.
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
-  int v = small_m ? 0 : 1;
-  v = env_int(gu ? "MOE_GEMM_VARIANT_GU" : "MOE_GEMM_VARIANT_DN", v);
-  hipError_t err = launch_variant(p, v, gu, q4, f32out, s);
-  if (err == hipErrorInvalidValue)                     // tile wider than N allows: narrower tiles
-    err = launch_variant(p, small_m ? 0 : 2, gu, q4, f32out, s);
-  return err;
-}
-
-static hipError_t launch_variant(const GemmParams& p, int v, bool gu, bool q4, bool f32out, hipStream_t s) {
-  // Tile shapes: rows x columns per tile for gate/up | down, waves, LDS buffers, workgroups per CU.
-  //   0 (decode):          32x64   | 32x128,  4 waves (1x4), 1 buffer,  4/CU (dense down: 2/CU), two
-  //                        chunks in registers
-  //   1 (prefill):         256x128 | 256x256, 8 waves (4x2), 2 buffers, 1/CU; dense weights: direct
-  //                        global -> LDS loads (down, up to 64 experts: three weight buffers);
-  //                        int4: one chunk in registers (dequantised on the way)
-  //   2 (prefill, narrow): 256x64  | 256x128, 4 waves (4x1), 2 buffers, 1/CU, two chunks in registers
-  const bool n256 = p.N % 256 == 0;
   if (gu) {
-    switch (v) {
-      case 0: return run_gu<32, 64, 1, 4, 1, 4>(p, q4, s);
-      case 1: return q4 ? run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, s) : run_dma<DCfg<256, 128, 4, 2, true>, u16>(p, s);
-      default: return run_gu<256, 64, 4, 1, 2, 1>(p, q4, s);
-    }
+    if (small_m) return run_gu<32, 64, 1, 4, 1, 4>(p, q4, s);
+    if (p.N % 128 == 0)
+      return q4 ? run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, s) : run_dma<DCfg<256, 128, 4, 2, true>, u16>(p, s);
+    return run_gu<256, 64, 4, 1, 2, 1>(p, q4, s);
   }
-  switch (v) {
-    case 0:
-      // dense: two workgroups per CU (half as many weight streams, each workgroup streams several
-      // tiles back to back): 2 % faster than four on the decode-shaped down projection
-      return q4 ? run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, s) : run_dn<32, 128, 1, 4, 1, 2>(p, q4, f32out, s);
-    case 1: {
-      if (!n256) return hipErrorInvalidValue;
-      if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s);
-      // three weight buffers (up to 64 experts: the tile table then fits in registers)
-      const hipError_t e = f32out ? run_dma3<DCfg<256, 256, 4, 2, false>, float>(p, s)
-                                  : run_dma3<DCfg<256, 256, 4, 2, false>, u16>(p, s);
-      if (e != hipErrorInvalidValue) return e;
-      return f32out ? run_dma<DCfg<256, 256, 4, 2, false>, float>(p, s) : run_dma<DCfg<256, 256, 4, 2, false>, u16>(p, s);
-    }
-    default: return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, s);
-  }
+  if (small_m)
+    // dense: two workgroups per CU (half as many weight streams, each workgroup streams several
+    // tiles back to back): 2 % faster than four on the decode-shaped down projection
+    return q4 ? run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, s) : run_dn<32, 128, 1, 4, 1, 2>(p, q4, f32out, s);
+  if (p.N % 256 != 0) return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, s);
+  if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s);
+  using D = DCfg<256, 256, 4, 2, false>;
+  if (p.n_groups <= 64)                                // tile table in registers: three weight buffers
+    return f32out ? run_dma3<D, float>(p, s) : run_dma3<D, u16>(p, s);
+  return f32out ? run_dma<D, float>(p, s) : run_dma<D, u16>(p, s);
 }
 
 }  // namespace moe
