@@ -48,6 +48,9 @@ MOE_API const char* moe_status_string(int status) {
     case MOE_ERR_INVALID_ARG: return "invalid argument";
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "input needs more scratch than the allocation-free entry point holds "
+             "(MOE_PERMUTE_NOALLOC_SCRATCH_BYTES per GPU); call moe_permute with a workspace";
     default: return "unknown status";
   }
 }

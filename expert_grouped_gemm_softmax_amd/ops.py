@@ -98,6 +98,20 @@ def permute(blob: torch.Tensor, e_first: int, e_local: int, sorted_pairs=None, g
     return sp, off, pp
 
 
+def permute_noalloc(blob: torch.Tensor, e_first: int, e_local: int, sorted_pairs: torch.Tensor,
+                    group_offsets: torch.Tensor, pair_pos: torch.Tensor, stream=None):
+    """permute() without a workspace, for callers that cannot allocate: the library keeps the
+    per-chunk counts in its own fixed device array (moe_permute_noalloc).  The output tensors are
+    the caller's; nothing is allocated here."""
+    _, T, k = blob.shape
+    assert blob.dtype == torch.int32
+    _dev(blob, sorted_pairs, group_offsets, pair_pos)
+    assert sorted_pairs.numel() >= T * k and pair_pos.numel() >= T * k and group_offsets.numel() >= e_local + 1
+    check("moe_permute_noalloc", load().moe_permute_noalloc(_ptr(blob), T, k, e_first, e_local, _ptr(sorted_pairs),
+                                                            _ptr(group_offsets), _ptr(pair_pos), _stream(stream)))
+    return sorted_pairs, group_offsets, pair_pos
+
+
 def prepare_dense_weights(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Dense weights [E][K][N] (x @ W) -> the same values stored [E][N][K] (MOE_W_DENSE_NK), the
     layout the bf16 grouped GEMM reads.  A one-time preparation, run by the library."""

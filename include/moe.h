@@ -44,7 +44,8 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,   /* null pointer, size out of range, inconsistent sizes */
   MOE_ERR_UNSUPPORTED = 2,   /* well-formed request outside what the library implements */
-  MOE_ERR_HIP = 3            /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_SCRATCH_TOO_SMALL = 4  /* moe_permute_noalloc: the input needs more than its fixed scratch */
 } moe_status;
 
 typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
@@ -134,6 +135,23 @@ size_t moe_permute_workspace_bytes(int T, int k, int e_local);
 moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
                        int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * outputs and limits as moe_permute, without the workspace: the per-chunk counts live in a
+ * library-owned static device array of MOE_PERMUTE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held
+ * until the process ends.  Allocates nothing.  Inputs whose moe_permute_workspace_bytes exceeds
+ * that size return MOE_ERR_SCRATCH_TOO_SMALL (e.g. 64 local experts: up to 8,388,608 pairs; 1024
+ * local experts: up to 524,288 pairs).  Every call on a GPU shares its array, which keeps the last
+ * call's contents (no call reads them): calls that overlap on one GPU (different streams or
+ * threads) race and must be serialised by the caller.
+ */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+moe_status moe_permute_noalloc(const int32_t* blob, int T, int k, int e_first, int e_local,
+                               int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
+                               void* stream);
 
 /*
  * moe_grouped_gemm -- one grouped GEMM over the experts of this device ("Systems engineering

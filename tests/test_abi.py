@@ -35,8 +35,9 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.moe_abi_version() == 1
-    for s in range(4):
+    for s in range(5):
         assert L.moe_status_string(s)
+    assert b"scratch" in L.moe_status_string(_abi.MOE_ERR_SCRATCH_TOO_SMALL)
     assert L.moe_status_string(99) == b"unknown status"
 
 
@@ -94,6 +95,26 @@ def test_pack_and_permute_validation(L):
     assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, None, ws, None) == INV
     assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == INV
     assert L.moe_permute(FAKE, 2049, 8, 0, 8, FAKE, FAKE, FAKE, FAKE + 4, ws, None) == INV   # alignment
+
+
+def test_permute_noalloc_validation(L):
+    """Host checks of the allocation-free permutation, including inputs whose per-chunk counts
+    would not fit its fixed scratch array (all rejected before any HIP call)."""
+    F = FAKE
+    TOO_BIG = _abi.MOE_ERR_SCRATCH_TOO_SMALL
+    assert L.moe_permute_noalloc(None, 2049, 8, 0, 8, F, F, F, None) == INV
+    assert L.moe_permute_noalloc(F, 2049, 8, 0, 8, None, F, F, None) == INV
+    assert L.moe_permute_noalloc(F, 2049, 8, 0, 8, F, None, F, None) == INV
+    assert L.moe_permute_noalloc(F, 2049, 8, 0, 8, F, F, None, None) == INV
+    assert L.moe_permute_noalloc(F, 0, 8, 0, 8, F, F, F, None) == INV
+    assert L.moe_permute_noalloc(F, 2049, 65, 0, 8, F, F, F, None) == INV
+    assert L.moe_permute_noalloc(F, 2049, 8, -1, 8, F, F, F, None) == INV
+    assert L.moe_permute_noalloc(F, 2049, 8, 0, 1025, F, F, F, None) == INV
+    cap = _abi.MOE_PERMUTE_NOALLOC_SCRATCH_BYTES
+    # 1024 local experts: 1024 chunks of 512 pairs fit exactly, one more chunk does not
+    assert L.moe_permute_workspace_bytes(1024 * 512 // 64, 64, 1024) == cap
+    assert L.moe_permute_noalloc(F, 1024 * 512 // 64 + 8, 64, 0, 1024, F, F, F, None) == TOO_BIG
+    assert L.moe_permute_noalloc(F, (1 << 23) // 64 + 8, 64, 0, 64, F, F, F, None) == TOO_BIG
 
 
 def _gemm(**kw):
