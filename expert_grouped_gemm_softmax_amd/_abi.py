@@ -9,8 +9,8 @@ from .build import LIB_PATH, INCLUDE
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_SCRATCH_TOO_SMALL = 0, 1, 2, 3, 4
 MOE_PERMUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
-MOE_DT_F32, MOE_DT_BF16 = 0, 1
-MOE_W_DENSE, MOE_W_INT4_SYM_GROUP, MOE_W_DENSE_NK = 0, 1, 2
+MOE_DT_F32, MOE_DT_BF16, MOE_DT_F16 = 0, 1, 2
+MOE_W_DENSE, MOE_W_INT4_SYM_GROUP, MOE_W_DENSE_NK, MOE_W_DENSE_NK_F16 = 0, 1, 2, 3
 MOE_OP_GATE_UP_SWIGLU, MOE_OP_DOWN = 0, 1
 
 
@@ -61,9 +61,10 @@ def load(path: str = LIB_PATH):
     L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), vp]
     L.moe_combine.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp]
     L.moe_prepare_dense_weights.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    L.moe_prepare_dense_weights_f16.argtypes = [vp, i32, i32, i32, vp, vp]
     for fn in ("moe_route", "moe_pack_routing", "moe_route_packed", "moe_permute", "moe_permute_noalloc",
                "moe_grouped_gemm",
-               "moe_combine", "moe_prepare_dense_weights"):
+               "moe_combine", "moe_prepare_dense_weights", "moe_prepare_dense_weights_f16"):
         getattr(L, fn).restype = i32
     _lib = L
     return L

@@ -97,17 +97,17 @@ MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, i
                                       pair_pos, workspace, as_stream(stream)); });
 }
 
+inline bool is_dtype(int d) { return d == MOE_DT_F32 || d == MOE_DT_BF16 || d == MOE_DT_F16; }
+
 MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->op != MOE_OP_GATE_UP_SWIGLU && a->op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
-  if (a->act_dtype != MOE_DT_F32 && a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-  if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP && a->wfmt != MOE_W_DENSE_NK)
+  if (!is_dtype(a->act_dtype) || !is_dtype(a->out_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP && a->wfmt != MOE_W_DENSE_NK &&
+      a->wfmt != MOE_W_DENSE_NK_F16)
     return MOE_ERR_UNSUPPORTED;
   const bool gu = a->op == MOE_OP_GATE_UP_SWIGLU;
-  if (a->out_dtype != a->act_dtype && !(a->out_dtype == MOE_DT_F32 && !gu)) {
-    if (a->out_dtype != MOE_DT_F32 && a->out_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-    return MOE_ERR_INVALID_ARG;
-  }
+  const bool q4 = a->wfmt == MOE_W_INT4_SYM_GROUP;
   if (!a->a || !a->group_offsets || !a->w0 || !a->out) return MOE_ERR_INVALID_ARG;
   if (gu ? !a->w1 : a->w1 != nullptr) return MOE_ERR_INVALID_ARG;
   if (a->K < 64 || a->K % 64 != 0 || a->N < 64) return MOE_ERR_INVALID_ARG;
@@ -115,21 +115,33 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (a->n_groups < 1 || a->n_groups > 1024) return MOE_ERR_INVALID_ARG;
   if (a->rows_cap < 1 || a->a_rows < 1 || a->row_div < 1 || a->m_hint < 0) return MOE_ERR_INVALID_ARG;
   if (!a->row_index && a->a_rows < a->rows_cap) return MOE_ERR_INVALID_ARG;
+  if (q4) {
+    if (!a->s0 || (gu && !a->s1)) return MOE_ERR_INVALID_ARG;
+  } else if (a->group_size != 0 || a->s0 || a->s1) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  // dtype combinations (see moe.h): an output dtype the op never writes is an invalid argument,
+  // a well-formed combination that is not implemented is unsupported
+  if (a->act_dtype == MOE_DT_F32) {
+    if (a->out_dtype != MOE_DT_F32) return MOE_ERR_INVALID_ARG;
+    if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_DENSE_NK) return MOE_ERR_UNSUPPORTED;
+  } else if (gu) {
+    if (a->out_dtype == MOE_DT_F32) return MOE_ERR_INVALID_ARG;
+    if (a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+    if (q4 ? a->out_dtype != MOE_DT_F16 : a->wfmt != MOE_W_DENSE_NK) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (a->out_dtype != MOE_DT_F32 && a->out_dtype != a->act_dtype) return MOE_ERR_INVALID_ARG;
+    if (a->act_dtype == MOE_DT_BF16 ? a->wfmt != MOE_W_DENSE_NK
+                                    : (a->wfmt != MOE_W_DENSE_NK_F16 && !q4))
+      return MOE_ERR_UNSUPPORTED;
+  }
   // 32-bit byte offsets inside a (below 2^31: offsets from 2^31 up mark rows that load nothing)
   // and inside one expert's weight matrix
   const long long esz = a->act_dtype == MOE_DT_F32 ? 4 : 2;
   if ((long long)a->a_rows * a->K * esz >= (1LL << 31) || (long long)a->K * a->N * esz >= (1LL << 32))
     return MOE_ERR_UNSUPPORTED;
-  if (a->wfmt == MOE_W_INT4_SYM_GROUP) {
-    if (a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-    if (a->group_size < 64 || a->group_size % 64 != 0 || a->K % a->group_size != 0)
-      return MOE_ERR_UNSUPPORTED;
-    if (!a->s0 || (gu && !a->s1)) return MOE_ERR_INVALID_ARG;
-  } else if (a->group_size != 0 || a->s0 || a->s1) {
-    return MOE_ERR_INVALID_ARG;
-  } else if (a->wfmt == MOE_W_DENSE && a->act_dtype == MOE_DT_BF16) {
-    return MOE_ERR_UNSUPPORTED;                        // prepare with moe_prepare_dense_weights
-  }
+  if (q4 && (a->group_size < 64 || a->group_size % 64 != 0 || a->K % a->group_size != 0))
+    return MOE_ERR_UNSUPPORTED;
   return enqueue([&] { return moe::launch_grouped_gemm(*a, as_stream(stream)); });
 }
 
@@ -142,11 +154,18 @@ MOE_API moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N,
   return enqueue([&] { return moe::launch_prepare(w, E, K, N, dtype, out, as_stream(stream)); });
 }
 
+MOE_API moe_status moe_prepare_dense_weights_f16(const void* w, int E, int K, int N, void* out, void* stream) {
+  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || K < 1 || N < 1 || E > 65535 || K > (1 << 22) || (long long)E * K * N >= (1LL << 40))
+    return MOE_ERR_INVALID_ARG;
+  return enqueue([&] { return moe::launch_prepare(w, E, K, N, MOE_DT_F16, out, as_stream(stream)); });
+}
+
 MOE_API moe_status moe_combine(const void* expert_out, int expert_rows, int act_dtype, const int32_t* blob,
                                const int32_t* pair_pos, const void* shared_out, int T, int k, int H,
                                void* y, int y_dtype, void* stream) {
   if (!expert_out || !blob || !pair_pos || !y) return MOE_ERR_INVALID_ARG;
-  if (act_dtype != MOE_DT_F32 && act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!is_dtype(act_dtype)) return MOE_ERR_UNSUPPORTED;
   if (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (expert_rows < 1 || T < 1 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;

@@ -33,6 +33,18 @@ template <> struct Vec8<u16> {
     __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
   }
 };
+template <> struct Vec8<_Float16> {
+  // halves taken with integer shifts: hipcc (ROCm 7.2) miscompiles element reads of a 16-bit
+  // vector bitcast from one dword of a 16-byte load (every element came from the same dword)
+  __device__ static void load(const _Float16* p, float* v) {
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = (float)__builtin_bit_cast(_Float16, (u16)(q[i] & 0xffffu));
+      v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (u16)(q[i] >> 16));
+    }
+  }
+};
 template <> struct Vec8<float> {
   __device__ static void load(const float* p, float* v) {
     const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
@@ -121,6 +133,9 @@ hipError_t launch_combine(const void* o, int act, const int32_t* blob, const int
   if (act == MOE_DT_BF16)
     return y_dtype == MOE_DT_BF16 ? run<u16, u16>(o, blob, pair_pos, shared, T, k, H, rows, y, s)
                                   : run<u16, float>(o, blob, pair_pos, shared, T, k, H, rows, y, s);
+  if (act == MOE_DT_F16)
+    return y_dtype == MOE_DT_BF16 ? run<_Float16, u16>(o, blob, pair_pos, shared, T, k, H, rows, y, s)
+                                  : run<_Float16, float>(o, blob, pair_pos, shared, T, k, H, rows, y, s);
   return y_dtype == MOE_DT_BF16 ? run<float, u16>(o, blob, pair_pos, shared, T, k, H, rows, y, s)
                                 : run<float, float>(o, blob, pair_pos, shared, T, k, H, rows, y, s);
 }

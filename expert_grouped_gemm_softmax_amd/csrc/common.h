@@ -10,6 +10,8 @@ namespace moe {
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -26,6 +28,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ u16 f32_to_bf16(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+
+// Round-to-nearest-even fp32 -> fp16 pair packed into one dword (lo in bits 0..15): one
+// v_cvt_pk_f16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// fp16 operands of the grouped GEMM carry weights scaled by 2^8 (int4 dequantisation and the
+// prepared fp16 dense weights), which centres fp16's exact range on weight magnitudes; outputs
+// are multiplied by 2^-8 (exact).
+constexpr float kF16WeightScale = 256.0f;
 
 // Host-side launchers (one per source file); each returns hipSuccess or the launch error.
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* blob,

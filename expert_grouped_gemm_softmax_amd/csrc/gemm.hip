@@ -21,8 +21,12 @@
 //    operands read (8 consecutive k per lane).
 //    int4 words [e][k/8][n] hold 8 consecutive k of one column: they are dequantised
 //    (q * scale, rounded to bf16) into the same [n][k] LDS layout.
-//  - v_mfma_f32_16x16x32_bf16 with fp32 accumulators; SwiGLU fused in the epilogue (each lane
-//    holds the gate and the up value of the same output element).
+//  - 16x16x32 MFMA with fp32 accumulators; SwiGLU fused in the epilogue (each lane holds the gate
+//    and the up value of the same output element).  Operands are bf16 (dense bf16 weights) or
+//    fp16: int4 weights are dequantised exactly to fp16 (q * s has at most 11 significant bits;
+//    a bf16 tile would round it), bf16 activations feeding them are converted to fp16 on their
+//    way to LDS, and the down projection reads the fp16 SwiGLU output with fp16 weights.  fp16
+//    weights carry a factor 2^8 that the epilogue removes.
 //  - Global loads run ahead of the MFMAs through registers (one or two chunks) and one or two
 //    LDS buffers.
 #include "common.h"
@@ -121,8 +125,26 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fdividef(g, 1.0f + __expf(-g)) * u;
 }
 
+// One 16x16x32 MFMA on 16-byte operand registers: bf16 or fp16 inputs, fp32 accumulation.
+template <bool F16>
+__device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+// Output element stores: fp32, bf16 (u16 bits) or fp16, rounded to nearest even.
+template <typename OutT>
+__device__ __forceinline__ void store_out(OutT* dst, float v) {
+  if constexpr (sizeof(OutT) == 4) *dst = v;
+  else if constexpr (__is_same(OutT, _Float16)) *dst = (_Float16)v;
+  else *dst = f32_to_bf16(v);
+}
+
 // ---------------------------------------------------------------------------------------------
-// bf16 MFMA kernel
+// MFMA kernel with register-staged loads
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kLdsPerCu = 160 * 1024;             // LDS of one gfx950 compute unit
 
@@ -134,8 +156,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1, int REGSETS_ = 2>
+// F16_: fp16 MFMA operands (weights scaled by 2^8); ACVT_: the activation matrix is bf16 and is
+// converted to fp16 on its way to LDS.  int4 weights always run on fp16 operands.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1, int REGSETS_ = 2,
+          bool F16_ = Q4_, bool ACVT_ = false>
 struct Cfg {
+  static constexpr bool F16 = F16_, ACVT = ACVT_;
+  static constexpr float OUT_MUL = F16_ ? 1.0f / kF16WeightScale : 1.0f;
   // Chunks held in registers between their loads and their LDS stores (two LDS buffers only).
   static constexpr int REGSETS = REGSETS_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
@@ -166,20 +193,19 @@ struct Cfg {
   static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * NT) == 0, "B tile split");
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
   static_assert(Q4 || BN % SLICE_ROWS == 0, "a dense piece slice stays inside one weight matrix");
+  static_assert(!Q4 || F16, "int4 weights are dequantised to fp16");
+  static_assert(!ACVT || F16, "activations are converted to the fp16 operand type");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
 
 // LDS tiles hold one 128-byte row (64 consecutive k) per activation row or weight column, in
-// 16-byte chunks; chunk q of row n sits at position q ^ swz(n).  The MFMA operand reads (16
-// consecutive rows, one chunk per 16-lane group) are free of bank conflicts because swz runs over
-// 0..7 on the even and on the odd rows of every 16-row block.  Activation tiles and dense weight
-// tiles use swz(n) = (n/2) mod 8, a function of n mod 16 only: all operand reads and row writes
-// of a lane are then one base register plus immediate offsets.  int4 weight tiles also XOR in
-// (n/16) mod 8, which keeps their dequantised column writes at most 2-way conflicted.
+// 16-byte chunks; chunk q of row n sits at position q ^ swz(n) with swz(n) = (n/2) mod 8.  The MFMA
+// operand reads (16 consecutive rows, one chunk per 16-lane group) are free of bank conflicts
+// because swz runs over 0..7 on the even and on the odd rows of every 16-row block, and since swz
+// depends on n mod 16 only, all operand reads of a lane are one base register plus immediate
+// offsets.  Dequantised int4 columns are written so that each 16-lane pass fills 8 chunks of an
+// even row and 8 of an odd row (see the int4 unit mapping), also without conflicts.
 __device__ __forceinline__ int lds_off_rows(int n, int q) { return n * 64 + ((q ^ ((n >> 1) & 7)) << 3); }
-__device__ __forceinline__ int lds_off_q4(int n, int q) {
-  return n * 64 + ((q ^ ((n >> 1) & 7) ^ ((n >> 4) & 7)) << 3);
-}
 
 // Registers holding one K chunk in flight: the activation rows and the weight units of this
 // thread.
@@ -212,8 +238,8 @@ struct TileCtx {
   int b_lds;                                        // dense: LDS destination of the lane's first piece
   uint32_t b_off[C::B_UNITS];                       // int4: word offset of the unit
   uint32_t s_off[C::B_UNITS];                       // int4: scale offset of the unit
-  int b_row[C::B_UNITS];                            // int4: first LDS row (weight column) of the unit
-  int b_q[C::B_UNITS];                              // int4: 16-byte chunk of the unit
+  int b_dst[C::B_UNITS][C::Q4 ? 4 : 1];             // int4: LDS destination of each dequantised column
+  bool b_swap[C::B_UNITS];                          // int4: columns written in swapped pairs
   int nK, row_bytes, s_row_bytes, group_size;
 };
 
@@ -250,11 +276,51 @@ __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& c
   }
 }
 
+// bf16 -> fp16 of eight packed values (exact for magnitudes in fp16's normal range).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xffff0000u));
+  return r;
+}
+
 template <class C>
 __device__ __forceinline__ void store_a(const TileCtx<C>& t, const AChunk<C>& ch, u16* buf) {
   u16* sA = buf;
 #pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) *reinterpret_cast<u32x4*>(sA + t.a_lds + C::SLICE_ROWS * i * 64) = ch.a[i];
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    u32x4 v = ch.a[i];
+    if constexpr (C::ACVT) v = bf16x8_to_f16x8(v);
+    *reinterpret_cast<u32x4*>(sA + t.a_lds + C::SLICE_ROWS * i * 64) = v;
+  }
+}
+
+// Eight int4 weights (the nibbles of one word, k ascending) times their scale, exactly, as eight
+// fp16 values: nibble u (two's complement q) -> u ^ 8 = q + 8, which placed in the low mantissa
+// bits of fp16 1024 gives 1032 + q; subtracting 1032 leaves q exactly, and q * (s * 2^8) has at
+// most 3 + 8 significant bits, so the packed fp16 product is exact.  Dword i holds the weights of
+// k = 2i (low half) and 2i + 1.
+__device__ __forceinline__ u32x4 dequant_int4_f16(uint32_t word, f16x2 scale2) {
+  const uint32_t w = word ^ 0x88888888u;
+  const uint32_t lo = w & 0x0f0f0f0fu;             // nibbles 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;      // nibbles 1, 3, 5, 7
+  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // bytes: lo byte i, 0, hi byte i, 0 (v_perm_b32 selector 0x0c yields a zero byte)
+    const uint32_t sel = 0x0c000c00u | (uint32_t)i | ((uint32_t)(4 + i) << 16);
+    const uint32_t t = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    const f16x2 q = __builtin_bit_cast(f16x2, t) - bias;
+    r[i] = __builtin_bit_cast(uint32_t, q * scale2);
+  }
+  return r;
+}
+
+// bf16 scale bits -> fp16 pair of the scale times 2^8 (exact for 2^-22 <= s < 32)
+__device__ __forceinline__ f16x2 scale_f16x2(uint32_t sbits) {
+  const _Float16 h = (_Float16)(__uint_as_float(sbits << 16) * kF16WeightScale);
+  return f16x2{h, h};
 }
 
 template <class C>
@@ -269,17 +335,11 @@ __device__ __forceinline__ void store_w(const TileCtx<C>& t, const WChunk<C>& ch
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t word = ch.b[i][0][c];
-        const uint32_t sbits = (c & 1) ? (ch.s[i][c >> 1] >> 16) : (ch.s[i][c >> 1] & 0xffffu);
-        const float sc = __uint_as_float(sbits << 16);
-        uint32_t q[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int q0 = ((int)(word << (28 - 8 * h))) >> 28;        // nibble 2h
-          const int q1 = ((int)(word << (24 - 8 * h))) >> 28;        // nibble 2h+1
-          q[h] = pack_bf16x2((float)q0 * sc, (float)q1 * sc);
-        }
-        *reinterpret_cast<u32x4*>(sB + lds_off_q4(t.b_row[i] + c, t.b_q[i])) = u32x4{q[0], q[1], q[2], q[3]};
+        // column c of the unit, or c ^ 1 for units written in swapped pairs
+        const uint32_t word = t.b_swap[i] ? ch.b[i][0][c ^ 1] : ch.b[i][0][c];
+        const uint32_t sdw = ch.s[i][c >> 1];
+        const uint32_t sbits = ((c & 1) != (int)t.b_swap[i]) ? (sdw >> 16) : (sdw & 0xffffu);
+        *reinterpret_cast<u32x4*>(sB + t.b_dst[i][c]) = dequant_int4_f16(word, scale_f16x2(sbits));
       }
     }
   }
@@ -308,23 +368,25 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
     const u16* sB = buf + C::A_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < C::KC; ks += 32) {
-      bf16x8 av[NM];
+      u32x4 av[NM];
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         const int off = lds_off_rows(arow, (ks + kofs) >> 3) + i * 16 * C::WM * 64;
-        av[i] = *reinterpret_cast<const bf16x8*>(sA + off);
+        av[i] = *reinterpret_cast<const u32x4*>(sA + off);
       }
 #pragma unroll
-      for (int m = 0; m < C::NW; ++m)
+      for (int m = 0; m < C::NW; ++m) {
 #pragma unroll
         for (int j = 0; j < C::NTL; ++j) {
-          const int off = C::Q4 ? lds_off_q4(m * C::BN + bcol + j * 16, (ks + kofs) >> 3)
-                                : lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64;
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sB + off);
+          const int off = lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64;
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(sB + off);
 #pragma unroll
-          for (int i = 0; i < NM; ++i)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv, acc[m][i][j], 0, 0, 0);
+          for (int i = 0; i < NM; ++i) acc[m][i][j] = mma<C::F16>(av[i], bv, acc[m][i][j]);
         }
+        // int4 prefill tiles: the operand reads of the next matrix and k-step stay behind these
+        // MFMAs (hoisted, they would hold more operand registers next to the dequantised chunk's)
+        if constexpr (C::Q4 && C::NWAVES == 8) __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -423,11 +485,9 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < rows) {
           float v;
-          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
-          else v = acc[0][i][j][r];
-          OutT* dst = O + (size_t)(row0 + row) * N + n0 + col;
-          if constexpr (sizeof(OutT) == 4) *dst = v;
-          else *dst = f32_to_bf16(v);
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
+          else v = acc[0][i][j][r] * C::OUT_MUL;
+          store_out(O + (size_t)(row0 + row) * N + n0 + col, v);
         }
       }
 }
@@ -501,8 +561,13 @@ void k_gemm_bf16(GemmParams p) {
       t.b_soff = (uint32_t)((n0 + wave * 8) * t.row_bytes);
       t.b_lds = lds_off_rows(wave * 8 + (lane >> 3), lane & 7);
     } else {
-      // Unit i of a thread (one 16-byte row piece: 4 words of 8 k each) reads matrix
-      // (tid + NT*i) / per_m, the same for the whole wave.
+      // Unit i of a thread (one 16-byte row piece: 4 words of 8 k each, columns 4 nq .. 4 nq + 3 of
+      // word row kw) reads matrix (tid + NT*i) / per_m, the same for the whole wave.  Within a
+      // matrix, unit u covers kw = u % 8 and nq = u / 8: the 16 lanes of an LDS pass hold 8 word
+      // rows of 2 adjacent column quads (nq even, nq odd), and a wave's loads are 8 whole 128-byte
+      // rows.  Odd quads write their columns in the order 1, 0, 3, 2, so at every store the two
+      // halves of a pass write rows of opposite parity: 8 chunks of an even row and 8 of an odd
+      // row, one per bank group.
       constexpr int per_m = KC * BN / 32;
       static_assert(per_m % 64 == 0, "a wave's units read one matrix");
 #pragma unroll
@@ -516,12 +581,14 @@ void k_gemm_bf16(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < C::B_UNITS; ++i) {
         const int u = (tid + NT * i) % per_m;
-        const int nq = u % (BN / 4), kw = u / (BN / 4);
+        const int kw = u % (KC / 8), nq = u / (KC / 8);
         const int m = (tid + NT * i) / per_m;
+        const int sw = nq & 1;
         t.b_off[i] = (uint32_t)(kw * p.N + n0 + nq * 4) * 4u;
         t.s_off[i] = (uint32_t)(n0 + nq * 4) * 2u;
-        t.b_row[i] = m * BN + nq * 4;
-        t.b_q[i] = kw;
+        t.b_swap[i] = sw != 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t.b_dst[i][c] = lds_off_rows(m * BN + nq * 4 + (c ^ sw), kw);
       }
     }
     tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0);
@@ -576,11 +643,9 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[C::NW][NA][C::NTL]
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < rows) {
           float v;
-          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
-          else v = acc[0][i][j][r];
-          OutT* dst = O + (size_t)(row0 + row) * N + n0 + col;
-          if constexpr (sizeof(OutT) == 4) *dst = v;
-          else *dst = f32_to_bf16(v);
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
+          else v = acc[0][i][j][r] * C::OUT_MUL;
+          store_out(O + (size_t)(row0 + row) * N + n0 + col, v);
         }
       }
 }
@@ -690,10 +755,12 @@ void k_gemm_stream(GemmParams p) {
 // LDS read, which serialises the pipeline): the kernel waits for them itself (s_waitcnt vmcnt(0)
 // before the barrier that publishes a buffer; vector memory operations of a wave complete in
 // issue order, and any other outstanding vector memory operation only makes the wait longer).
-template <int BM_, int BN_, int WM_, int WN_, bool GU_>
+// F16_: fp16 operands (activations already fp16, weights carrying 2^8), else bf16.
+template <int BM_, int BN_, int WM_, int WN_, bool GU_, bool F16_ = false>
 struct DCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr bool GU = GU_;
+  static constexpr bool GU = GU_, F16 = F16_;
+  static constexpr float OUT_MUL = F16_ ? 1.0f / kF16WeightScale : 1.0f;
   static constexpr int NWAVES = WM * WN, NT = 64 * NWAVES;
   static constexpr int WAVES_PER_SIMD = (NWAVES + 3) / 4;
   static constexpr int KC = 64, NW = GU ? 2 : 1;
@@ -765,17 +832,17 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
       // Every operand of the chunk is read before its MFMAs: LDS reads return in order, so each
       // MFMA waits only for its own operands and the later reads overlap the earlier MFMAs.
       constexpr int KS = C::KC / 32;
-      bf16x8 av[KS][NM], bv[KS][C::NW][C::NTL];
+      u32x4 av[KS][NM], bv[KS][C::NW][C::NTL];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int i = 0; i < NM; ++i)
-          av[ks][i] = *reinterpret_cast<const bf16x8*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
+          av[ks][i] = *reinterpret_cast<const u32x4*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
 #pragma unroll
         for (int m = 0; m < C::NW; ++m)
 #pragma unroll
           for (int j = 0; j < C::NTL; ++j)
-            bv[ks][m][j] = *reinterpret_cast<const bf16x8*>(sB + lds_off_rows(bcol, (ks * 32 + kofs) >> 3) + (m * C::BN + j * 16) * 64);
+            bv[ks][m][j] = *reinterpret_cast<const u32x4*>(sB + lds_off_rows(bcol, (ks * 32 + kofs) >> 3) + (m * C::BN + j * 16) * 64);
       }
       __builtin_amdgcn_sched_barrier(0);           // keep the reads ahead of the MFMAs
 #pragma unroll
@@ -786,7 +853,7 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
           for (int j = 0; j < C::NTL; ++j)
 #pragma unroll
             for (int i = 0; i < NM; ++i)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks][i], bv[ks][m][j], acc[m][i][j], 0, 0, 0);
+              acc[m][i][j] = mma<C::F16>(av[ks][i], bv[ks][m][j], acc[m][i][j]);
     }
   }
   __syncthreads();
@@ -800,11 +867,9 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < tc.rows) {
           float v;
-          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
-          else v = acc[0][i][j][r];
-          OutT* dst = O + (size_t)(tc.row0 + row) * N + tc.n0 + col;
-          if constexpr (sizeof(OutT) == 4) *dst = v;
-          else *dst = f32_to_bf16(v);
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
+          else v = acc[0][i][j][r] * C::OUT_MUL;
+          store_out(O + (size_t)(tc.row0 + row) * N + tc.n0 + col, v);
         }
       }
 }
@@ -978,17 +1043,17 @@ __device__ __forceinline__ void dma3_tile(const DmaCtx<C>& t, u16* smem, OutT* O
       const u16* sA = smem + (kc & 1) * C::A_ELEMS;
       const u16* sB = smem + 2 * C::A_ELEMS + sb * C::B_ELEMS;
       constexpr int KS = C::KC / 32;
-      bf16x8 av[KS][NM], bv[KS][C::NW][C::NTL];
+      u32x4 av[KS][NM], bv[KS][C::NW][C::NTL];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int i = 0; i < NM; ++i)
-          av[ks][i] = *reinterpret_cast<const bf16x8*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
+          av[ks][i] = *reinterpret_cast<const u32x4*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
 #pragma unroll
         for (int m = 0; m < C::NW; ++m)
 #pragma unroll
           for (int j = 0; j < C::NTL; ++j)
-            bv[ks][m][j] = *reinterpret_cast<const bf16x8*>(sB + lds_off_rows(bcol, (ks * 32 + kofs) >> 3) + (m * C::BN + j * 16) * 64);
+            bv[ks][m][j] = *reinterpret_cast<const u32x4*>(sB + lds_off_rows(bcol, (ks * 32 + kofs) >> 3) + (m * C::BN + j * 16) * 64);
       }
       __builtin_amdgcn_sched_barrier(0);           // keep the reads ahead of the MFMAs
 #pragma unroll
@@ -999,7 +1064,7 @@ __device__ __forceinline__ void dma3_tile(const DmaCtx<C>& t, u16* smem, OutT* O
           for (int j = 0; j < C::NTL; ++j)
 #pragma unroll
             for (int i = 0; i < NM; ++i)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks][i], bv[ks][m][j], acc[m][i][j], 0, 0, 0);
+              acc[m][i][j] = mma<C::F16>(av[ks][i], bv[ks][m][j], acc[m][i][j]);
     }
     sb = sb == 2 ? 0 : sb + 1;
   }
@@ -1014,11 +1079,9 @@ __device__ __forceinline__ void dma3_tile(const DmaCtx<C>& t, u16* smem, OutT* O
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < tc.rows) {
           float v;
-          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r], acc[1][i][j][r]);
-          else v = acc[0][i][j][r];
-          OutT* dst = O + (size_t)(tc.row0 + row) * N + tc.n0 + col;
-          if constexpr (sizeof(OutT) == 4) *dst = v;
-          else *dst = f32_to_bf16(v);
+          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
+          else v = acc[0][i][j][r] * C::OUT_MUL;
+          store_out(O + (size_t)(tc.row0 + row) * N + tc.n0 + col, v);
         }
       }
 }
@@ -1254,25 +1317,58 @@ constexpr bool cfg_ok() {
          (A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0) && BM / WM >= 16 && BN / WN >= 16;
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
-hipError_t run_gu(const GemmParams& p, bool q4, hipStream_t s) {
+// Output dtypes of one launch (the ABI's checks leave these combinations):
+//   gate/up: bf16 activations; h in bf16 or fp16 (dense weights: bf16 operands; int4: fp16
+//            operands, activations converted); int4 needs fp16 h;
+//   down:    bf16 h with bf16 weights (bf16 operands) or fp16 h with fp16 or int4 weights (fp16
+//            operands); out in fp32 or h's dtype.
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS, bool Q4, bool F16, typename OutT>
+hipError_t run_cfg_gu(const GemmParams& p, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, true>(), "gate/up tile");
-  static_assert(Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>::STAGES * Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>::STAGE * 2 +
-                    2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
-  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, true, true, WGS, RS>, u16>(p, WGS, s)
-            : run_bf16<Cfg<BM, BN, WM, WN, ST, true, false, WGS, RS>, u16>(p, WGS, s);
+  using C = Cfg<BM, BN, WM, WN, ST, true, Q4, WGS, RS, F16, F16>;
+  static_assert(C::STAGES * C::STAGE * 2 + 2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
+  return run_bf16<C, OutT>(p, WGS, s);
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS = 2>
-hipError_t run_dn(const GemmParams& p, bool q4, bool f32out, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS, bool Q4, bool F16, typename OutT>
+hipError_t run_cfg_dn(const GemmParams& p, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, false>(), "down tile");
-  static_assert(Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>::STAGES * Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>::STAGE * 2 +
-                    2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
-  if (f32out)
-    return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, float>(p, WGS, s)
-              : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, float>(p, WGS, s);
-  return q4 ? run_bf16<Cfg<BM, BN, WM, WN, ST, false, true, WGS, RS>, u16>(p, WGS, s)
-            : run_bf16<Cfg<BM, BN, WM, WN, ST, false, false, WGS, RS>, u16>(p, WGS, s);
+  using C = Cfg<BM, BN, WM, WN, ST, false, Q4, WGS, RS, F16, false>;
+  static_assert(C::STAGES * C::STAGE * 2 + 2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
+  return run_bf16<C, OutT>(p, WGS, s);
+}
+
+// gate/up, one tile shape: int4 on fp16 operands (h fp16), or dense bf16 (h bf16 or fp16)
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS>
+hipError_t run_gu_q4(const GemmParams& p, hipStream_t s) {
+  return run_cfg_gu<BM, BN, WM, WN, ST, WGS, RS, true, true, _Float16>(p, s);
+}
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS>
+hipError_t run_gu(const GemmParams& p, bool q4, bool h16, hipStream_t s) {
+  if (q4) return run_gu_q4<BM, BN, WM, WN, ST, WGS, RS>(p, s);
+  return h16 ? run_cfg_gu<BM, BN, WM, WN, ST, WGS, RS, false, false, _Float16>(p, s)
+             : run_cfg_gu<BM, BN, WM, WN, ST, WGS, RS, false, false, u16>(p, s);
+}
+
+// down, one tile shape: operands bf16 (dense bf16) or fp16 (h fp16 with fp16 or int4 weights)
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS>
+hipError_t run_dn(const GemmParams& p, bool q4, bool f16, bool f32out, hipStream_t s) {
+  if (q4)
+    return f32out ? run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, true, true, float>(p, s)
+                  : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, true, true, _Float16>(p, s);
+  if (f16)
+    return f32out ? run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, true, float>(p, s)
+                  : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, true, _Float16>(p, s);
+  return f32out ? run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, false, float>(p, s)
+                : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, false, u16>(p, s);
+}
+
+// dense prefill-shaped down projection with direct global -> LDS loads
+template <bool F16, typename OutT>
+hipError_t run_dma_dn(const GemmParams& p, hipStream_t s) {
+  using D = DCfg<256, 256, 4, 2, false, F16>;
+  if (p.n_groups <= 64) return run_dma3<D, OutT>(p, s);   // tile table in registers: three weight buffers
+  return run_dma<D, OutT>(p, s);
 }
 
 }  // namespace
@@ -1290,25 +1386,30 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
               : (nk ? run_f32<false, true>(p, s) : run_f32<false, false>(p, s));
   }
   const bool q4 = a.wfmt == MOE_W_INT4_SYM_GROUP;
+  const bool f16 = q4 || a.act_dtype == MOE_DT_F16;    // fp16 operands
   const bool f32out = a.out_dtype == MOE_DT_F32;
+  const bool h16 = a.out_dtype == MOE_DT_F16;
   // The ABI guarantees N % 64 == 0 (gate/up) and N % 128 == 0 (down): variants 0 and 2 always fit.
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
   if (gu) {
-    if (small_m) return run_gu<32, 64, 1, 4, 1, 4>(p, q4, s);
-    if (p.N % 128 == 0)
-      return q4 ? run_gu<256, 128, 4, 2, 2, 1, 1>(p, q4, s) : run_dma<DCfg<256, 128, 4, 2, true>, u16>(p, s);
-    return run_gu<256, 64, 4, 1, 2, 1>(p, q4, s);
+    if (small_m) return run_gu<32, 64, 1, 4, 1, 4, 2>(p, q4, h16, s);
+    if (p.N % 128 == 0) {
+      // int4: 192-row tiles (256 rows need more than the 256 registers of two waves per SIMD)
+      if (q4) return run_gu_q4<192, 128, 4, 2, 2, 1, 1>(p, s);
+      return h16 ? run_dma<DCfg<256, 128, 4, 2, true>, _Float16>(p, s) : run_dma<DCfg<256, 128, 4, 2, true>, u16>(p, s);
+    }
+    return run_gu<256, 64, 4, 1, 2, 1, 2>(p, q4, h16, s);
   }
-  if (small_m)
+  if (small_m) {
     // dense: two workgroups per CU (half as many weight streams, each workgroup streams several
     // tiles back to back): 2 % faster than four on the decode-shaped down projection
-    return q4 ? run_dn<32, 128, 1, 4, 1, 4>(p, q4, f32out, s) : run_dn<32, 128, 1, 4, 1, 2>(p, q4, f32out, s);
-  if (p.N % 256 != 0) return run_dn<256, 128, 4, 1, 2, 1>(p, q4, f32out, s);
-  if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f32out, s);
-  using D = DCfg<256, 256, 4, 2, false>;
-  if (p.n_groups <= 64)                                // tile table in registers: three weight buffers
-    return f32out ? run_dma3<D, float>(p, s) : run_dma3<D, u16>(p, s);
-  return f32out ? run_dma<D, float>(p, s) : run_dma<D, u16>(p, s);
+    if (q4) return run_dn<32, 128, 1, 4, 1, 4, 2>(p, q4, f16, f32out, s);
+    return run_dn<32, 128, 1, 4, 1, 2, 2>(p, q4, f16, f32out, s);
+  }
+  if (p.N % 256 != 0) return run_dn<256, 128, 4, 1, 2, 1, 2>(p, q4, f16, f32out, s);
+  if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f16, f32out, s);
+  if (f16) return f32out ? run_dma_dn<true, float>(p, s) : run_dma_dn<true, _Float16>(p, s);
+  return f32out ? run_dma_dn<false, float>(p, s) : run_dma_dn<false, u16>(p, s);
 }
 
 }  // namespace moe

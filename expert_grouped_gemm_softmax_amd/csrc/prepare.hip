@@ -1,6 +1,7 @@
 // One-time weight preparation for gfx950: dense expert matrices as the layer states them,
 // W[e][k][n] (x·W), are stored transposed as W[e][n][k] -- the [out][in] orientation in which the
-// grouped GEMM reads each output column's K weights as one contiguous row.
+// grouped GEMM reads each output column's K weights as one contiguous row -- in their own dtype, or
+// from bf16 to fp16 holding 2^8 * W for the fp16 down projection.
 //
 // 64 x 64 tiles through LDS: a workgroup reads 64 rows of 64 consecutive n (coalesced), and
 // writes 64 rows of 64 consecutive k (coalesced); the LDS tile is padded by one element per row so
@@ -10,7 +11,17 @@
 namespace moe {
 namespace {
 
-template <typename T>
+// Element conversions: identity, or bf16 bits -> fp16 bits of 2^8 times the value.
+struct Same {
+  template <typename T> __device__ static T cvt(T v) { return v; }
+};
+struct Bf16ToF16Scaled {
+  __device__ static u16 cvt(u16 b) {
+    return __builtin_bit_cast(u16, (_Float16)(__uint_as_float((uint32_t)b << 16) * kF16WeightScale));
+  }
+};
+
+template <typename T, class Cvt>
 __global__ __launch_bounds__(256) void k_prepare(const T* __restrict__ w, int K, int N, T* __restrict__ out) {
   __shared__ T tile[64][64 + 1];
   const int e = blockIdx.z;
@@ -18,16 +29,14 @@ __global__ __launch_bounds__(256) void k_prepare(const T* __restrict__ w, int K,
   const T* src = w + (size_t)e * K * N;
   T* dst = out + (size_t)e * N * K;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
-#pragma unroll
   for (int r = ty; r < 64; r += 4) {
     const int k = k0 + r, n = n0 + tx;
     if (k < K && n < N) tile[r][tx] = src[(size_t)k * N + n];
   }
   __syncthreads();
-#pragma unroll
   for (int r = ty; r < 64; r += 4) {
     const int n = n0 + r, k = k0 + tx;
-    if (n < N && k < K) dst[(size_t)n * K + k] = tile[tx][r];
+    if (n < N && k < K) dst[(size_t)n * K + k] = Cvt::cvt(tile[tx][r]);
   }
 }
 
@@ -35,10 +44,12 @@ __global__ __launch_bounds__(256) void k_prepare(const T* __restrict__ w, int K,
 
 hipError_t launch_prepare(const void* w, int E, int K, int N, int dtype, void* out, hipStream_t s) {
   const dim3 grid((N + 63) / 64, (K + 63) / 64, E), block(256);
-  if (dtype == MOE_DT_BF16)
-    k_prepare<u16><<<grid, block, 0, s>>>(static_cast<const u16*>(w), K, N, static_cast<u16*>(out));
+  if (dtype == MOE_DT_F16)                         // bf16 in, fp16 (x 2^8) out
+    k_prepare<u16, Bf16ToF16Scaled><<<grid, block, 0, s>>>(static_cast<const u16*>(w), K, N, static_cast<u16*>(out));
+  else if (dtype == MOE_DT_BF16)
+    k_prepare<u16, Same><<<grid, block, 0, s>>>(static_cast<const u16*>(w), K, N, static_cast<u16*>(out));
   else
-    k_prepare<float><<<grid, block, 0, s>>>(static_cast<const float*>(w), K, N, static_cast<float*>(out));
+    k_prepare<float, Same><<<grid, block, 0, s>>>(static_cast<const float*>(w), K, N, static_cast<float*>(out));
   return hipGetLastError();
 }
 

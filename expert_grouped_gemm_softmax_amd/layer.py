@@ -16,10 +16,11 @@ class ExpertWeights:
     """Device-resident weights of the local experts (and of the optional shared expert).
 
     A layer weight W is K x N (output n = sum_k a[k] W[k][n]); K = H, N = I for gate/up and the
-    reverse for down.  Dense weights are held prepared, [e_local][N][K] in the activation dtype
-    (MOE_W_DENSE_NK, written by the library from the stated [e_local][K][N]; see upload):
-    w_gate, w_up [e_local][I][H], w_down [e_local][H][I]; shared expert gate, up [Is][H], down [H][Is].
-    int4: int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N]."""
+    reverse for down.  Dense weights are held prepared, [e_local][N][K] (written by the library
+    from the stated [e_local][K][N]; see upload): w_gate, w_up [e_local][I][H] in the activation
+    dtype, w_down [e_local][H][I] in the dtype of the SwiGLU output h (fp16 holding 2^8 * W by
+    default, or bf16); shared expert gate, up [Is][H], down [H][Is] likewise.
+    int4: int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N]; h is fp16."""
     w_gate: torch.Tensor
     w_up: torch.Tensor
     w_down: torch.Tensor
@@ -35,6 +36,12 @@ class ExpertWeights:
     def int4(self) -> bool:
         return self.w_gate.dtype == torch.int32
 
+    @property
+    def h_dtype(self) -> torch.dtype:
+        """dtype of the SwiGLU output h between the two GEMMs: fp16 over fp16 or int4 down weights
+        (the fp16 MFMA path), else the down weights' dtype."""
+        return torch.float16 if self.int4 else self.w_down.dtype
+
 
 def _t(a: np.ndarray, device) -> torch.Tensor:
     """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
@@ -43,14 +50,23 @@ def _t(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def upload(inputs: dict, cfg, device="cuda") -> tuple[torch.Tensor, torch.Tensor, ExpertWeights]:
+def upload(inputs: dict, cfg, device="cuda", h_dtype=torch.float16) -> tuple[torch.Tensor, torch.Tensor, ExpertWeights]:
     """Copy a workloads.make_inputs() dict to the GPU -> (x, logits, weights).  Dense weights
-    arrive [E][K][N] and are prepared once by the library (moe_prepare_dense_weights)."""
+    arrive [E][K][N] and are prepared once by the library: gate/up with moe_prepare_dense_weights,
+    the down projections of a bf16 layer with moe_prepare_dense_weights_f16 when h_dtype is fp16
+    (the default: h rounded to fp16, 8x finer than bf16) or moe_prepare_dense_weights for bf16 h."""
     x = _t(inputs["x"], device)
     logits = _t(inputs["logits"], device)
+    assert h_dtype in (torch.float16, torch.bfloat16)
 
     def dense(name):
         return ops.prepare_dense_weights(_t(inputs[name], device))
+
+    def dense_down(name):
+        w = _t(inputs[name], device)
+        if w.dtype == torch.bfloat16 and h_dtype == torch.float16:
+            return ops.prepare_dense_weights_f16(w)
+        return ops.prepare_dense_weights(w)
 
     if cfg.wfmt == "int4":
         kw = dict(w_gate=_t(inputs["w_gate"], device), w_up=_t(inputs["w_up"], device),
@@ -58,9 +74,10 @@ def upload(inputs: dict, cfg, device="cuda") -> tuple[torch.Tensor, torch.Tensor
                   s_gate=_t(inputs["w_gate_scale"], device), s_up=_t(inputs["w_up_scale"], device),
                   s_down=_t(inputs["w_down_scale"], device), group_size=cfg.group_size)
     else:
-        kw = dict(w_gate=dense("w_gate"), w_up=dense("w_up"), w_down=dense("w_down"))
+        kw = dict(w_gate=dense("w_gate"), w_up=dense("w_up"), w_down=dense_down("w_down"))
     if cfg.shared_I:
-        kw.update(shared_gate=dense("shared_gate"), shared_up=dense("shared_up"), shared_down=dense("shared_down"))
+        kw.update(shared_gate=dense("shared_gate"), shared_up=dense("shared_up"),
+                  shared_down=dense_down("shared_down"))
     return x, logits, ExpertWeights(**kw)
 
 
@@ -96,12 +113,18 @@ class MoELayer:
         # every row would add an error proportional to |y| on top of the bf16 GEMM operands.
         self.o_dtype = torch.float32
         self.y_dtype = y_dtype
+        self.h_dtype = weights.h_dtype if act_dtype == torch.bfloat16 else act_dtype
         self.shared_I = 0 if weights.shared_gate is None else weights.shared_gate.shape[0]
         self._check_shapes()
         self._buf: dict[int, Buffers] = {}
 
     def _check_shapes(self):
         W, H, I, el = self.weights, self.H, self.I, self.e_local
+        if W.shared_down is not None and not W.int4 and W.shared_down.dtype != W.w_down.dtype:
+            raise ValueError("shared and routed down projections need one h dtype")
+        if W.int4 and W.shared_down is not None and W.shared_down.dtype != torch.float16:
+            raise ValueError("an int4 layer's shared down projection reads fp16 h: prepare it with "
+                             "prepare_dense_weights_f16")
         if W.int4:
             want = {"w_gate": (el, H // 8, I), "w_up": (el, H // 8, I), "w_down": (el, I // 8, H)}
         else:
@@ -127,18 +150,17 @@ class MoELayer:
         if b is None:
             k, cap = self.k, self.rows_capacity(T)
             i32 = dict(dtype=torch.int32, device=device)
-            act = dict(dtype=self.act_dtype, device=device)
             b = Buffers(ids=torch.empty((T, k), **i32), w=torch.empty((T, k), dtype=torch.float32, device=device),
                         blob=torch.empty((2, T, k), **i32), sorted_pairs=torch.empty(T * k, **i32),
                         group_offsets=torch.empty(self.e_local + 1, **i32), pair_pos=torch.empty(T * k, **i32),
-                        h=torch.empty((cap, self.I), **act),
+                        h=torch.empty((cap, self.I), dtype=self.h_dtype, device=device),
                         o=torch.empty((cap, self.H), dtype=self.o_dtype, device=device),
                         y=torch.empty((T, self.H), dtype=self.y_dtype, device=device))
             b.workspace = torch.empty(max(1, ops.permute_workspace_bytes(T, k, self.e_local)),
                                       dtype=torch.uint8, device=device)
             if self.shared_I:
                 b.shared_offsets = torch.tensor([0, T], **i32)
-                b.shared_h = torch.empty((T, self.shared_I), **act)
+                b.shared_h = torch.empty((T, self.shared_I), dtype=self.h_dtype, device=device)
                 b.shared_o = torch.empty((T, self.H), dtype=self.o_dtype, device=device)
             self._buf[T] = b
         return b

@@ -13,7 +13,7 @@ import torch
 from . import _abi
 from ._abi import check, load
 
-_DT = {torch.float32: _abi.MOE_DT_F32, torch.bfloat16: _abi.MOE_DT_BF16}
+_DT = {torch.float32: _abi.MOE_DT_F32, torch.bfloat16: _abi.MOE_DT_BF16, torch.float16: _abi.MOE_DT_F16}
 
 
 def _stream(stream) -> int:
@@ -126,13 +126,29 @@ def prepare_dense_weights(w: torch.Tensor, out: torch.Tensor | None = None, stre
     return out[0] if squeeze else out
 
 
+def prepare_dense_weights_f16(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 dense weights [E][K][N] -> fp16 [E][N][K] holding 2^8 * w (MOE_W_DENSE_NK_F16), the
+    weights of a down projection over fp16 h.  A one-time preparation, run by the library."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    E, K, N = w3.shape
+    assert w3.is_contiguous() and w3.dtype == torch.bfloat16
+    out = out if out is not None else torch.empty((E, N, K), dtype=torch.float16, device=w.device)
+    assert out.dtype == torch.float16 and tuple(out.shape) == (E, N, K)
+    _dev(w3, out)
+    check("moe_prepare_dense_weights_f16", load().moe_prepare_dense_weights_f16(_ptr(w3), E, K, N, _ptr(out),
+                                                                                _stream(stream)))
+    return out[0] if squeeze else out
+
+
 def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torch.Tensor,
                  w1: torch.Tensor | None, out: torch.Tensor, *, K: int, N: int, row_index=None,
                  row_div: int = 1, s0=None, s1=None, group_size: int = 0, m_hint: int = 0,
                  weights_nk: bool = True, stream=None):
     """One grouped GEMM (see moe_grouped_gemm in include/moe.h).  Dense weights are
     [n_groups][N][K] (weights_nk, from prepare_dense_weights) or [n_groups][K][N] (fp32 only) in the
-    activation dtype; int4 weights are int32 words [n_groups][K/8][N] with bf16 scales s0/s1
+    activation dtype, or fp16 [n_groups][N][K] from prepare_dense_weights_f16 (down projection over
+    fp16 h); int4 weights are int32 words [n_groups][K/8][N] with bf16 scales s0/s1
     [n_groups][K/group_size][N]."""
     _dev(a, group_offsets, w0, w1, out, row_index, s0, s1)
     args = _abi.MoeGemmArgs()
@@ -140,6 +156,8 @@ def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torc
     args.act_dtype = _DT[a.dtype]
     if w0.dtype == torch.int32:
         args.wfmt = _abi.MOE_W_INT4_SYM_GROUP
+    elif w0.dtype == torch.float16:
+        args.wfmt = _abi.MOE_W_DENSE_NK_F16
     else:
         args.wfmt = _abi.MOE_W_DENSE_NK if weights_nk else _abi.MOE_W_DENSE
     args.group_size = group_size if args.wfmt == _abi.MOE_W_INT4_SYM_GROUP else 0

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -48,12 +48,19 @@ typedef enum moe_status {
   MOE_ERR_SCRATCH_TOO_SMALL = 4  /* moe_permute_noalloc: the input needs more than its fixed scratch */
 } moe_status;
 
-typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+/* MOE_DT_F16 (IEEE binary16) is the dtype of the SwiGLU output h between the two grouped GEMMs of
+ * a bf16 layer: its 11-bit significand keeps the rounding of h 8x smaller than bf16's, which the
+ * layer's error bar needs on heavy-tailed outputs. */
+typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_F16 = 2 } moe_dtype;
 
 /* Expert weight formats for a K x N matrix W of expert e (output n = sum_k a[k] W[k][n]).
  * MOE_W_DENSE: W[e][k][n] in the activation dtype, the layout the layer is stated in.
  * MOE_W_DENSE_NK: the same values stored [e][n][k] (row n = the K weights of output n), as
  * moe_prepare_dense_weights writes them; the bf16 grouped GEMM reads this layout.
+ * MOE_W_DENSE_NK_F16: fp16 [e][n][k] holding 2^8 * W (moe_prepare_dense_weights_f16 writes it
+ * from bf16 MOE_W_DENSE weights), the weights of a down projection over fp16 h.  The conversion
+ * is exact for 2^-22 <= |W| <= 255 (fp16's normal range shifted by 2^8); smaller magnitudes keep
+ * an absolute error below 2^-33.
  * MOE_W_INT4_SYM_GROUP: symmetric int4 with one bf16 scale per group of
  * `group_size` consecutive K rows per output column ("vLLM TPU Inference v0.31.0", 4-bit weight
  * scope: symmetric int4, group-wise scales, activations not quantised; asymmetric, 8-bit and
@@ -61,7 +68,12 @@ typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
  * Layout for a [K][N] matrix of expert e: words int32 [E][K/8][N], the two's-complement nibble at
  * bits 4i..4i+3 of word [e][kb][n] is q[8*kb+i][n]; scales bf16 [E][K/group_size][N];
  * weight = q * scale.  Channel-wise scales are group_size == K. */
-typedef enum moe_wfmt { MOE_W_DENSE = 0, MOE_W_INT4_SYM_GROUP = 1, MOE_W_DENSE_NK = 2 } moe_wfmt;
+typedef enum moe_wfmt {
+  MOE_W_DENSE = 0,
+  MOE_W_INT4_SYM_GROUP = 1,
+  MOE_W_DENSE_NK = 2,
+  MOE_W_DENSE_NK_F16 = 3
+} moe_wfmt;
 
 typedef enum moe_gemm_op {
   MOE_OP_GATE_UP_SWIGLU = 0,  /* out = silu(A Wg) * (A Wu), silu(z) = z / (1 + e^-z) */
@@ -162,20 +174,27 @@ moe_status moe_permute_noalloc(const int32_t* blob, int T, int k, int e_first, i
  * A row a[row_index[r] / row_div] (or a[r] when row_index is NULL) and expert e's weights.
  * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg(e)[k][n]) * (sum_k A[k] Wu(e)[k][n]).
  * DOWN:           out[r][n] = sum_k A[k] Wd(e)[k][n].
- * Weight formats: bf16 activations take MOE_W_DENSE_NK (prepare MOE_W_DENSE weights once with
- * moe_prepare_dense_weights; MOE_W_DENSE itself is MOE_ERR_UNSUPPORTED there) or
- * MOE_W_INT4_SYM_GROUP; fp32 activations take MOE_W_DENSE or MOE_W_DENSE_NK.
- * bf16 path: bf16 operands, fp32 accumulation, bf16 or (DOWN) fp32 output; int4 weights are
- * dequantised to bf16 in LDS.  A bf16 DOWN output is the round-to-nearest-even of the fp32 one
- * (the same accumulators); against an exact evaluation it adds a relative error of up to 2^-9 per
- * element (layer max-abs error 1.5-2.8 % of the output RMS on dense bf16 weights, about 3 % on
- * int4 group-128 weights), so fp32 is the output meant for partial sums.  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are
+ * Supported combinations (anything else is MOE_ERR_UNSUPPORTED; MOE_W_DENSE with 16-bit
+ * activations is prepared once with moe_prepare_dense_weights[_f16]):
+ *   fp32:     a, weights (MOE_W_DENSE or MOE_W_DENSE_NK) and out fp32; vector-ALU fp32 arithmetic.
+ *   GATE_UP:  a = x bf16; MOE_W_DENSE_NK bf16 weights (bf16 MFMA operands) with out (h) bf16 or
+ *             fp16, or MOE_W_INT4_SYM_GROUP with out fp16.
+ *   DOWN:     a = h bf16 with MOE_W_DENSE_NK bf16 weights (bf16 operands), or a = h fp16 with
+ *             MOE_W_DENSE_NK_F16 or MOE_W_INT4_SYM_GROUP weights (fp16 operands); out fp32 or a's
+ *             dtype.
+ * Accumulation is fp32 throughout.  int4 weights run on fp16 operands: each weight q * s is
+ * dequantised exactly to fp16 in LDS (q * s has at most 11 significant bits, which bf16 would
+ * round), as 2^8 * q * s, exact for scales 2^-22 <= s < 32; their bf16 activations x are converted
+ * to fp16 on the way to LDS (exact for |x| in [2^-14, 65504]; smaller magnitudes keep an absolute
+ * error below 2^-25).  fp16 outputs (h) are rounded to nearest even and overflow to infinity above
+ * 65504.  A 16-bit DOWN output is the round-to-nearest-even of the fp32 one (the same
+ * accumulators); fp32 is the output meant for partial sums.  fp32 path: fp32 throughout.  Rows >= group_offsets[n_groups] are
  * not written.  Limits (32-bit byte offsets): a_rows * K * sizeof(act) < 2^31 and
  * K * N * sizeof(act) < 2^32, else MOE_ERR_UNSUPPORTED.
  */
 typedef struct moe_gemm_args {
   int32_t op;          /* moe_gemm_op */
-  int32_t act_dtype;   /* moe_dtype of a, out and dense weights */
+  int32_t act_dtype;   /* moe_dtype of a (and of dense MOE_W_DENSE / MOE_W_DENSE_NK weights) */
   int32_t wfmt;        /* moe_wfmt of w0 / w1 (int4 requires MOE_DT_BF16) */
   int32_t group_size;  /* int4: K rows per scale; a multiple of 64 that divides K.  Dense: 0 */
   int32_t K;           /* contraction length: H for GATE_UP, I for DOWN; multiple of 64 */
@@ -186,8 +205,7 @@ typedef struct moe_gemm_args {
   int32_t a_rows;      /* rows of a (tokens for GATE_UP, rows_cap for DOWN) */
   int32_t row_div;     /* >= 1; divisor applied to row_index (k for GATE_UP after moe_permute) */
   int32_t m_hint;      /* expected rows per group, a launch-shape hint only (0: unknown) */
-  int32_t out_dtype;   /* moe_dtype of out: act_dtype, or MOE_DT_F32 for DOWN (fp32 partial
-                          outputs avoid a bf16 rounding of every expert output row) */
+  int32_t out_dtype;   /* moe_dtype of out (see the combinations above) */
   const void* a;                 /* [a_rows][K] act dtype */
   const int32_t* row_index;      /* [rows_cap] (e.g. sorted_pairs) or NULL for identity rows */
   const int32_t* group_offsets;  /* [n_groups+1] non-decreasing, [0] = 0 (e.g. from moe_permute) */
@@ -209,6 +227,14 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, void* stream);
 moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N, int dtype, void* out, void* stream);
 
 /*
+ * moe_prepare_dense_weights_f16 -- one-time weight preparation for a down projection over fp16 h:
+ * out[e][n][k] = fp16(2^8 * w[e][k][n]) from bf16 MOE_W_DENSE weights, i.e. MOE_W_DENSE_NK_F16
+ * (exact for 2^-22 <= |w| <= 255; rounded to nearest even otherwise).  w and out must not overlap.
+ *   Limits: as moe_prepare_dense_weights.
+ */
+moe_status moe_prepare_dense_weights_f16(const void* w, int E, int K, int N, void* out, void* stream);
+
+/*
  * moe_combine -- weighted sum back to token order ("Systems engineering playbook ...",
  * executive summary: the unpermute building block; section 1: the always-executed shared expert
  * is added to the routed output, its formula being read as plain addition).
@@ -223,7 +249,7 @@ moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N, int dty
  *                                            order (deterministic, no atomics); a token with no
  *                                            local pair gets 0 (+ shared_out[t]).
  *   Limits: 1 <= T, 1 <= k <= 64, H a multiple of 8, 1 <= expert_rows, T * k < 2^31; act_dtype
- *   and y_dtype in {MOE_DT_F32, MOE_DT_BF16}.
+ *   in {MOE_DT_F32, MOE_DT_BF16, MOE_DT_F16}, y_dtype in {MOE_DT_F32, MOE_DT_BF16}.
  */
 moe_status moe_combine(const void* expert_out, int expert_rows, int act_dtype, const int32_t* blob,
                        const int32_t* pair_pos, const void* shared_out, int T, int k, int H,

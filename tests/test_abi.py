@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for s in range(5):
         assert L.moe_status_string(s)
     assert b"scratch" in L.moe_status_string(_abi.MOE_ERR_SCRATCH_TOO_SMALL)
@@ -138,9 +138,18 @@ def _gemm(**kw):
     (dict(n_groups=0), INV), (dict(n_groups=1025), INV), (dict(rows_cap=0), INV), (dict(a_rows=0), INV),
     (dict(row_div=0), INV), (dict(m_hint=-1), INV), (dict(row_index=None, a_rows=10), INV),
     (dict(wfmt=1, act_dtype=0, out_dtype=0, group_size=128, s0=FAKE, s1=FAKE), UNS),
-    (dict(wfmt=1, group_size=32, s0=FAKE, s1=FAKE), UNS),
-    (dict(wfmt=1, group_size=96, s0=FAKE, s1=FAKE), UNS),
-    (dict(wfmt=1, K=192, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, out_dtype=2, group_size=32, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, out_dtype=2, group_size=96, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, out_dtype=2, K=192, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    # int4 runs on fp16 operands: gate/up writes fp16 h, down reads fp16 h
+    (dict(wfmt=1, out_dtype=1, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    (dict(op=1, K=128, N=256, w1=None, wfmt=1, act_dtype=1, out_dtype=0, group_size=128, s0=FAKE), UNS),
+    # fp16 h over fp16 weights, bf16 h over bf16 weights; no fp16 gate/up input
+    (dict(op=1, K=128, N=256, w1=None, wfmt=3, act_dtype=1, out_dtype=0), UNS),
+    (dict(op=1, K=128, N=256, w1=None, wfmt=2, act_dtype=2, out_dtype=0), UNS),
+    (dict(op=1, K=128, N=256, w1=None, wfmt=3, act_dtype=2, out_dtype=1), INV),
+    (dict(act_dtype=2, out_dtype=2), UNS), (dict(wfmt=3, out_dtype=2), UNS),
+    (dict(act_dtype=0, out_dtype=0, wfmt=3), UNS),
     (dict(wfmt=1, group_size=128, s0=None, s1=FAKE), INV),
     (dict(wfmt=1, group_size=128, s0=FAKE, s1=None), INV),
     (dict(group_size=128), INV), (dict(s0=FAKE), INV),
@@ -160,7 +169,7 @@ def test_combine_validation(L):
         args = list(ok)
         args[i] = v
         assert L.moe_combine(*args) == INV, (i, v)
-    for i, v in [(2, 3), (10, 9)]:
+    for i, v in [(2, 3), (10, 9), (10, 2)]:
         args = list(ok)
         args[i] = v
         assert L.moe_combine(*args) == UNS, (i, v)
@@ -177,6 +186,18 @@ def test_prepare_dense_weights_validation(L):
     assert L.moe_prepare_dense_weights(F, 65536, 64, 64, 1, F, None) == INV
     assert L.moe_prepare_dense_weights(F, 1, (1 << 22) + 1, 64, 1, F, None) == INV
     assert L.moe_prepare_dense_weights(F, 1024, 1 << 15, 1 << 15, 1, F, None) == INV   # 2^40 elements
+
+
+def test_prepare_dense_weights_f16_validation(L):
+    F = FAKE
+    assert L.moe_prepare_dense_weights_f16(None, 2, 64, 64, F, None) == INV
+    assert L.moe_prepare_dense_weights_f16(F, 2, 64, 64, None, None) == INV
+    assert L.moe_prepare_dense_weights_f16(F, 0, 64, 64, F, None) == INV
+    assert L.moe_prepare_dense_weights_f16(F, 2, 0, 64, F, None) == INV
+    assert L.moe_prepare_dense_weights_f16(F, 2, 64, 0, F, None) == INV
+    assert L.moe_prepare_dense_weights_f16(F, 1024, 1 << 15, 1 << 15, F, None) == INV
+    # the bf16 -> fp16 preparation has its own entry point
+    assert L.moe_prepare_dense_weights(F, 2, 64, 64, 2, F, None) == UNS
 
 
 def test_calibration_library_exports_and_rejects_bad_sizes():

@@ -50,8 +50,8 @@ def _check_close(got, ref, what=""):
     assert mx <= MAX_ABS_RMS * rms, mx / rms
 
 
-def _run(cfg, inp, y_dtype=torch.float32, m_hint=None):
-    x, logits, wts = upload(inp, cfg, _dev())
+def _run(cfg, inp, y_dtype=torch.float32, m_hint=None, h_dtype=torch.float16):
+    x, logits, wts = upload(inp, cfg, _dev(), h_dtype=h_dtype)
     layer = MoELayer.from_config(cfg, wts, y_dtype=y_dtype)
     if m_hint is not None:
         layer.m_hint = lambda T: m_hint
@@ -233,15 +233,23 @@ MID = {
 }
 
 
+MID_BF16_H = [n for n, c in MID.items() if c.act == "bf16" and c.wfmt == "dense"]
+
+
 @pytest.mark.parametrize("variant", ["small_m", "large_m"])
-@pytest.mark.parametrize("name", list(MID))
-def test_layer_mid_size_every_token(name, variant):
+@pytest.mark.parametrize("name,h", [(n, "f16") for n in MID] + [(n, "bf16") for n in MID_BF16_H])
+def test_layer_mid_size_every_token(name, h, variant):
+    """Every token of the mid-size shapes on both tile families; bf16 layers with fp16 h (the
+    default) and, over bf16 down weights, with bf16 h."""
     cfg = MID[name]
     inp = W.make_inputs(cfg)
-    layer, b, y = _run(cfg, inp, y_dtype=torch.float32, m_hint=(8 if variant == "small_m" else 0))
+    h_dtype = torch.float16 if h == "f16" else torch.bfloat16
+    layer, b, y = _run(cfg, inp, y_dtype=torch.float32, m_hint=(8 if variant == "small_m" else 0), h_dtype=h_dtype)
+    if cfg.act == "bf16":
+        assert b.h.dtype == h_dtype
     ids, w, off = _check_routing(b, inp, cfg)
     ref = oracle.layer(inp, cfg, ids, w, threads=8)
-    _check_close(_np(y).astype(np.float64), ref, f"{name}/{variant}")
+    _check_close(_np(y).astype(np.float64), ref, f"{name}/{h}/{variant}")
     if not cfg.shared_I:
         counts = np.zeros(cfg.T, int)
         loc = (ids >= cfg.e_first) & (ids < cfg.e_first + cfg.e_local)
@@ -291,45 +299,40 @@ def test_layer_bf16_output_is_rounded_fp32_output_and_deterministic():
 
 
 @pytest.mark.parametrize("hint", [8, 1 << 20], ids=["decode_tiles", "prefill_tiles"])
-@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_skew_empty", "bf16_shared", "int4_g128"])
-def test_down_projection_bf16_output_and_bf16_combine(name, hint):
-    """DOWN with bf16 output rows is the round-to-nearest-even of its fp32 output (same
-    accumulators, only the epilogue's store differs), on both tile families; combine on bf16 rows
-    (and bf16 shared rows) matches the oracle within the layer bar on the dense shapes."""
+@pytest.mark.parametrize("name,h_dtype", [("bf16_ragged", torch.float16), ("bf16_ragged", torch.bfloat16),
+                                          ("bf16_skew_empty", torch.float16), ("bf16_shared", torch.float16),
+                                          ("bf16_shared", torch.bfloat16), ("int4_g128", torch.float16)])
+def test_down_projection_16bit_output_and_16bit_combine(name, h_dtype, hint):
+    """DOWN with 16-bit output rows (h's dtype) is the round-to-nearest-even of its fp32 output
+    (same accumulators, only the epilogue's store differs), on both tile families; combine on
+    those rows (and 16-bit shared rows) matches the oracle within the layer bar."""
     cfg = MID[name]
     inp = W.make_inputs(cfg)
-    x, logits, wts = upload(inp, cfg, _dev())
+    x, logits, wts = upload(inp, cfg, _dev(), h_dtype=h_dtype)
     layer = MoELayer.from_config(cfg, wts)
     layer.m_hint = lambda T: hint
     layer.forward(x, logits)
     b = layer.buffers(cfg.T, x.device)
+    assert b.h.dtype == h_dtype
     Wt = layer.weights
-    o16 = torch.empty(b.o.shape, dtype=torch.bfloat16, device=x.device)
+    o16 = torch.empty(b.o.shape, dtype=h_dtype, device=x.device)
     ops.grouped_gemm(1, b.h, b.group_offsets, Wt.w_down, None, o16, K=cfg.I, N=cfg.H, s0=Wt.s_down,
                      group_size=Wt.group_size, m_hint=hint)
     sh16 = None
     if cfg.shared_I:
-        sh16 = torch.empty(b.shared_o.shape, dtype=torch.bfloat16, device=x.device)
+        sh16 = torch.empty(b.shared_o.shape, dtype=h_dtype, device=x.device)
         ops.grouped_gemm(1, b.shared_h, b.shared_offsets, Wt.shared_down, None, sh16, K=cfg.shared_I, N=cfg.H,
                          m_hint=cfg.T)
     y = ops.combine(o16, b.blob, b.pair_pos, sh16, y_dtype=torch.float32)
     torch.cuda.synchronize()
     n = int(b.group_offsets[-1])
-    assert torch.equal(o16[:n].view(torch.int16), b.o[:n].to(torch.bfloat16).view(torch.int16))
+    bits = torch.int16
+    assert torch.equal(o16[:n].view(bits), b.o[:n].to(h_dtype).view(bits))
     if sh16 is not None:
-        assert torch.equal(sh16.view(torch.int16), b.shared_o.to(torch.bfloat16).view(torch.int16))
+        assert torch.equal(sh16.view(bits), b.shared_o.to(h_dtype).view(bits))
     ids, w = oracle.route(inp["logits"], cfg.k)
     ref = oracle.layer(inp, cfg, ids, w, threads=8)
-    rms = float(np.sqrt((ref ** 2).mean()))
-    got = _np(y).astype(np.float64)
-    if cfg.wfmt == "dense":
-        _check_close(got, ref, f"{name} bf16 o")
-    else:
-        # int4 weights already spend most of the max-abs budget on the bf16 rounding of the
-        # dequantised weights; with bf16 expert rows on top only the relative L2 bar is asserted
-        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-        print(f"{name} bf16 o: rel_l2={rel:.3e} max_abs/rms={np.abs(got - ref).max() / rms:.3e}")
-        assert rel <= REL_L2
+    _check_close(_np(y).astype(np.float64), ref, f"{name} h {h_dtype} 16-bit o")
 
 
 def test_layer_single_token_and_single_expert():
