@@ -2,11 +2,16 @@
 
 A step is one pass of the whole path (route -> pack -> permute -> gate/up GEMM + SwiGLU -> down
 GEMM [-> shared expert] -> combine) over one batch of synthetic inputs already resident in HBM.
-Prints ONE JSON line.  The default workload is the decode-shaped EP share (T=512 tokens, hidden
-4096, experts 0-63 of 512 local, top-10, intermediate 1024, bf16).
+Prints ONE JSON line.  The headline workload is the largest one that fits one GPU: Zipf-skewed
+routing plus a shared SwiGLU expert (T=8192 tokens, hidden 4096, experts 0-63 of 512 local, top-10,
+intermediate 1024, bf16).  The other four workloads (tiny fp32, decode, prefill, W4A16) are
+measured the same way, each in a child process of its own that runs before this process touches
+the GPU (so a profiler's per-process kernel statistics of this process cover the headline only),
+and reported under "workloads".
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-  python bench.py --copy-calibration      # plain device copy of known size (HBM counter scale)
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--cpu-seconds S]
+  python bench.py --workload NAME          # one workload only, as the headline
+  python bench.py --copy-calibration       # plain device copy of known size (HBM counter scale)
 """
 from __future__ import annotations
 
@@ -14,6 +19,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -21,9 +28,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "routed token-expert pairs/s + % of HBM/MFMA roofline, one device's MoE layer"
-EVENT_EVERY = 5                                    # timed steps per bracketed gate/up launch
+HEADLINE = "skewed_shared"
+SUBS = ["tiny", "decode", "prefill", "w4a16"]
+EVENT_EVERY = 5                # timed steps per event-bracketed launch of the dominant kernel
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix peak
+MFMA_16BIT_PEAK_TFS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
 FP32_PEAK_TFS = 157.3          # MI355X fp32 vector peak
 
 DESCR = {
@@ -60,44 +69,111 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def gemm_work(cfg, n_loc: int, nonempty: int, op: str):
-    """Algorithmic FLOPs and HBM bytes of one grouped-GEMM launch: every weight byte of the
-    experts that received pairs read once, activations read once, outputs written once."""
-    H, I, T = cfg.H, cfg.I, cfg.T
-    act = 2 if cfg.act == "bf16" else 4
-    out = 4                                   # expert outputs are written in fp32
+# ---------------------------------------------------------------------------------------------
+# Algorithmic work
+# ---------------------------------------------------------------------------------------------
+def weight_bytes(cfg, K: int, N: int) -> int:
+    """Bytes of one K x N expert matrix as stored in HBM (int4 words + bf16 scales, or dense)."""
     if cfg.wfmt == "int4":
-        wbytes = lambda K, N: K * N // 2 + (K // cfg.group_size) * N * 2
-    else:
-        wbytes = lambda K, N: K * N * act
-    if op == "gate_up":
-        flops = 4.0 * H * I * n_loc
-        byts = nonempty * 2 * wbytes(H, I) + T * H * act + n_loc * I * act
-    else:
-        flops = 2.0 * H * I * n_loc
-        byts = nonempty * wbytes(I, H) + n_loc * I * act + n_loc * H * out
-    return flops, byts
+        return K * N // 2 + (K // cfg.group_size) * N * 2
+    return K * N * (2 if cfg.act == "bf16" else 4)
 
 
-def roofline(cfg, flops: float, byts: float, seconds: float):
-    peak_f = MFMA_BF16_PEAK_TFS if cfg.act == "bf16" else FP32_PEAK_TFS
+def work(cfg, n_loc: int, nonempty: int) -> dict:
+    """Algorithmic flops and bytes: the layer (weights of the experts that received pairs, the
+    shared expert's weights, x read once, the router logits, y written once in fp32) and each
+    kernel (its weights and its reads of x; the implementation's own h and o round trips are
+    not algorithmic)."""
+    H, I, T, E, Is = cfg.H, cfg.I, cfg.T, cfg.E, cfg.shared_I
+    act = 2 if cfg.act == "bf16" else 4
+    x_b, logit_b, y_b = T * H * act, T * E * 4, T * H * 4
+    gu_w = nonempty * 2 * weight_bytes(cfg, H, I)
+    dn_w = nonempty * weight_bytes(cfg, I, H)
+    sh_w = 3 * H * Is * act
+    w = {
+        "gate_up": {"flops": 4.0 * H * I * n_loc, "bytes": gu_w + x_b},
+        "down": {"flops": 2.0 * H * I * n_loc, "bytes": dn_w},
+        "layer": {"flops": 6.0 * H * I * n_loc + 6.0 * H * Is * T,
+                  "bytes": gu_w + dn_w + sh_w + x_b + logit_b + y_b},
+    }
+    if Is:
+        w["shared"] = {"flops": 6.0 * H * Is * T, "bytes": sh_w + x_b}
+    return w
+
+
+def matrix_peak(cfg) -> float:
+    return MFMA_16BIT_PEAK_TFS if cfg.act == "bf16" else FP32_PEAK_TFS
+
+
+def roofline(cfg, flops: float, byts: float, seconds: float, att=None) -> dict:
+    """Achieved rate against the binding roofline (HBM if bytes/BW >= flops/peak, else the matrix
+    peak of the arithmetic dtype; fp32 arithmetic runs on the vector ALU) for work done in
+    `seconds`; frac_of_attainable against the measured ceilings when given."""
+    peak_f = matrix_peak(cfg)
     t_hbm = byts / (HBM_PEAK_GBS * 1e9)
     t_mat = flops / (peak_f * 1e12)
     if t_hbm >= t_mat:
         a = byts / seconds / 1e9
-        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4)}
-    a = flops / seconds / 1e12
-    return {"bound": "mfma" if cfg.act == "bf16" else "alu", "achieved": round(a, 1), "peak": peak_f,
-            "unit": "TFLOP/s", "frac": round(a / peak_f, 4)}
+        r = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(a / HBM_PEAK_GBS, 4)}
+        if att:
+            r["frac_of_attainable"] = round(a / att["hbm_read_gbs"], 4)
+    else:
+        a = flops / seconds / 1e12
+        r = {"bound": "mfma" if cfg.act == "bf16" else "alu", "achieved": round(a, 1), "peak": peak_f,
+             "unit": "TFLOP/s", "frac": round(a / peak_f, 4)}
+        if att and cfg.act == "bf16":
+            r["frac_of_attainable"] = round(a / att["mfma_bf16_tflops"], 4)
+    return r
+
+
+def layer_roofline(cfg, wk: dict, seconds: float) -> dict:
+    """max(B/BW, F/P) / t for the whole layer: the fraction of the layer's own roofline time."""
+    L = wk["layer"]
+    t_hbm = L["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mat = L["flops"] / (matrix_peak(cfg) * 1e12)
+    return {"bytes": int(L["bytes"]), "flops": int(L["flops"]), "t_hbm_us": round(t_hbm * 1e6, 1),
+            "t_matrix_us": round(t_mat * 1e6, 1), "bound": "hbm" if t_hbm >= t_mat else
+            ("mfma" if cfg.act == "bf16" else "alu"), "frac": round(max(t_hbm, t_mat) / seconds, 4)}
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores
+# ---------------------------------------------------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """Every core this process may use: its CPU affinity, capped by a cgroup CPU quota when one is
+    set, and by os.cpu_count()."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, -(-int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    return max(1, min(n, os.cpu_count() or n))
 
 
 def cpu_baseline(cfg, inp, budget_s: float):
-    """The CPU oracle on a bounded sample of the same workload's tokens (whole path for those
-    tokens: routing, blob, permutation, expert FFNs and combine)."""
+    """The CPU oracle on a bounded sample of the same workload's tokens (the whole path for those
+    tokens: routing, blob, permutation, expert FFNs and combine), one thread per usable core."""
     import numpy as np
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
 
     def run(tokens):
         t0 = time.perf_counter()
@@ -118,10 +194,14 @@ def cpu_baseline(cfg, inp, budget_s: float):
         dt, n_pairs = run(tokens)
         secs, pairs, reps = secs + dt, pairs + n_pairs, reps + 1
     return {"value": round(pairs / secs, 2), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{n} of {cfg.T} tokens drawn uniformly (seed 1), x{reps} repetitions, "
                       f"{pairs} local pairs in {secs:.1f} s on {threads} host threads"}
 
 
+# ---------------------------------------------------------------------------------------------
+# Measured ceilings
+# ---------------------------------------------------------------------------------------------
 def attainable_peaks():
     """Measured ceilings on this GPU, next to the published peaks: a bf16 MFMA loop that touches no
     memory and a streaming read of 2 GiB (well past the 256 MB last-level cache), each the best
@@ -184,50 +264,37 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 5}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-calibration", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
+# ---------------------------------------------------------------------------------------------
+# One workload
+# ---------------------------------------------------------------------------------------------
+def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -> dict:
+    """Time `steps` whole steps of one workload (after `warmup`), then per-step latencies and a
+    per-kernel breakdown in separate event-bracketed passes; rooflines; the CPU oracle."""
     import numpy as np
     import torch
     from expert_grouped_gemm_softmax_amd import workloads as W
     from expert_grouped_gemm_softmax_amd.layer import MoELayer, upload
 
-    cfg = W.CONFIGS[args.workload]
+    cfg = W.CONFIGS[name]
     t0 = time.perf_counter()
     inp = W.make_inputs(cfg, threads=16)
     x, logits, wts = upload(inp, cfg, torch.device("cuda:0"))
     layer = MoELayer.from_config(cfg, wts)
     b = layer.buffers(cfg.T, x.device)
-    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         layer.forward(x, logits)
     torch.cuda.synchronize()
     off = b.group_offsets.cpu().numpy()
     n_loc = int(off[-1])
     nonempty = int((np.diff(off) > 0).sum())
 
-    K = args.steps
+    K = steps
     stream = torch.cuda.current_stream()
     # Timed region: K whole steps between synchronisations; HIP events on the launch stream
-    # bracket the dominant kernel (the gate/up grouped GEMM) in every EVENT_EVERY-th step, from
-    # the first to the last timed step.  A recorded event costs about 3 us of stream time, so
-    # bracketing every step would add about 2.5 % to a decode step.
+    # bracket the dominant kernel (the routed gate/up grouped GEMM) in every EVENT_EVERY-th step,
+    # from the first to the last timed step (a recorded event costs about 3 us of stream time).
     sampled = list(range(0, K, EVENT_EVERY))
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
     torch.cuda.synchronize()
@@ -246,11 +313,10 @@ def main():
         layer.step_combine(b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per_kernel = {"gate_up": [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in sampled]}
+    gu_us = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in sampled]))
     ms_per_step = wall / K * 1e3
-    value = n_loc / (ms_per_step / 1e3)
 
-    # Layer latency, measured after the timed region: each step between two events of its own.
+    # Layer latency, after the timed region: each step between two events of its own.
     lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for i in range(K):
         lev[i][0].record(stream)
@@ -259,63 +325,121 @@ def main():
     torch.cuda.synchronize()
     step_us = np.array([lev[i][0].elapsed_time(lev[i][1]) * 1e3 for i in range(K)])
 
-    # Per-step breakdown, measured after the timed region (events between every step).
+    # Per-kernel breakdown, after the timed region (events between every step).
     names = ["route_pack_permute", "gate_up", "down"] + (["shared"] if cfg.shared_I else []) + ["combine"]
-    steps = [lambda: layer.step_route(logits, b), lambda: layer.step_gate_up(x, b),
-             lambda: layer.step_down(x, b)] + ([lambda: layer.step_shared(x, b)] if cfg.shared_I else []) + \
-            [lambda: layer.step_combine(b)]
+    fns = [lambda: layer.step_route(logits, b), lambda: layer.step_gate_up(x, b),
+           lambda: layer.step_down(x, b)] + ([lambda: layer.step_shared(x, b)] if cfg.shared_I else []) + \
+          [lambda: layer.step_combine(b)]
     nb = max(3, min(K, 10))
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nb)]
     for i in range(nb):
         bev[i][0].record(stream)
-        for j, fn in enumerate(steps):
+        for j, fn in enumerate(fns):
             fn()
             bev[i][j + 1].record(stream)
     torch.cuda.synchronize()
-    breakdown = {n: float(np.mean([bev[i][j].elapsed_time(bev[i][j + 1]) * 1e3 for i in range(nb)]))
-                 for j, n in enumerate(names)}
+    kus = {n: float(np.mean([bev[i][j].elapsed_time(bev[i][j + 1]) * 1e3 for i in range(nb)]))
+           for j, n in enumerate(names)}
 
-    gu_us = float(np.mean(per_kernel["gate_up"]))
-    flops, byts = gemm_work(cfg, n_loc, nonempty, "gate_up")
-    roof = roofline(cfg, flops, byts, gu_us * 1e-6)
-    roof["kernel"] = "grouped GEMM gate/up + SwiGLU"
-    roof["algorithmic_bytes"] = int(byts)
-    roof["algorithmic_flops"] = int(flops)
-    roof["traffic"] = measured_traffic(args.workload, "gate_up")
-    dn_us = breakdown["down"]
-    dflops, dbytes = gemm_work(cfg, n_loc, nonempty, "down")
-    layer_flops = flops + dflops
-    layer_bytes = byts + dbytes
-
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "pairs/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.act == "bf16" else "f32",
-        "data": "synthetic: seeded normal activations, random-init expert weights, fp32 router logits",
-        "config": {"workload": DESCR[args.workload], "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
-                   "I": cfg.I, "e_local": cfg.e_local, "weights": cfg.wfmt, "shared_I": cfg.shared_I},
-        "roofline": roof,
-        "roofline_samples": len(sampled),
-        "n_local_pairs": n_loc,
-        "latency_us": {"median": round(float(np.median(step_us)), 1),
-                       "p10": round(float(np.percentile(step_us, 10)), 1),
+    wk = work(cfg, n_loc, nonempty)
+    roof = roofline(cfg, wk["gate_up"]["flops"], wk["gate_up"]["bytes"], gu_us * 1e-6, att)
+    roof.update({"kernel": "routed grouped GEMM gate/up + SwiGLU", "time_us": round(gu_us, 1),
+                 "algorithmic_bytes": int(wk["gate_up"]["bytes"]), "algorithmic_flops": int(wk["gate_up"]["flops"]),
+                 "traffic": measured_traffic(name, "gate_up"), "samples": len(sampled)})
+    kernels = {"down": roofline(cfg, wk["down"]["flops"], wk["down"]["bytes"], kus["down"] * 1e-6, att)}
+    if cfg.shared_I:
+        kernels["shared"] = roofline(cfg, wk["shared"]["flops"], wk["shared"]["bytes"], kus["shared"] * 1e-6, att)
+    pair_s = n_loc / (ms_per_step / 1e3)
+    res = {
+        "workload": name, "description": DESCR[name],
+        "config": {"T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I, "e_local": cfg.e_local,
+                   "weights": cfg.wfmt, "act": cfg.act, "shared_I": cfg.shared_I},
+        "ms_per_step": round(ms_per_step, 4), "pairs_per_s": round(pair_s, 1), "steps": K, "warmup": warmup,
+        "timed_region_s": round(wall, 4), "n_local_pairs": n_loc, "nonempty_experts": nonempty,
+        "latency_us": {"p10": round(float(np.percentile(step_us, 10)), 1),
+                       "median": round(float(np.median(step_us)), 1),
                        "p90": round(float(np.percentile(step_us, 90)), 1)},
-        "kernels_us": {n: round(v, 1) for n, v in breakdown.items()},
-        "down_roofline": roofline(cfg, dflops, dbytes, dn_us * 1e-6),
-        "gemm_pair_roofline": roofline(cfg, layer_flops, layer_bytes, (gu_us + dn_us) * 1e-6),
+        "layer_roofline": layer_roofline(cfg, wk, ms_per_step * 1e-3),
+        "roofline": roof,
+        "kernels_us": {n: round(v, 1) for n, v in kus.items()},
+        "kernel_rooflines": kernels,
     }
-    att = attainable_peaks()
-    out["attainable"] = att
-    if att:
-        if roof["unit"] == "GB/s":
-            roof["frac_of_attainable"] = round(roof["achieved"] / att["hbm_read_gbs"], 4)
-        elif roof["bound"] == "mfma":
-            roof["frac_of_attainable"] = round(roof["achieved"] / att["mfma_bf16_tflops"], 4)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    if cpu_s:
+        print(f"[bench] {name}: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, cpu_s)
     else:
-        out["cpu_baseline"] = None
+        res["cpu_baseline"] = None
+    del layer, b, x, logits, wts
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_child(name: str, args) -> dict:
+    """One sub-workload in a child process of its own (this process has not touched the GPU)."""
+    cmd = [sys.executable, "-u", os.path.abspath(__file__), "--child", "--workload", name,
+           "--steps", str(args.steps), "--warmup", str(args.warmup), "--cpu-seconds", str(args.cpu_seconds)]
+    if args.no_cpu_baseline:
+        cmd.append("--no-cpu-baseline")
+    print(f"[bench] child: {name}", file=sys.stderr, flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"bench child for {name} failed with exit code {r.returncode}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="measure this workload only (as the headline)")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    cpu_s = None if args.no_cpu_baseline else args.cpu_seconds
+    if args.child:
+        print(json.dumps(measure(args.workload, args.steps, args.warmup, cpu_s)), flush=True)
+        return
+
+    print(f"[bench] pid {os.getpid()}", file=sys.stderr, flush=True)
+    head = args.workload or HEADLINE
+    subs = {} if args.workload else {n: run_child(n, args) for n in SUBS}   # before this process uses the GPU
+
+    att = attainable_peaks()
+    h = measure(head, args.steps, args.warmup, None if cpu_s is None else max(cpu_s, 12.0), att)
+    for r in subs.values():                       # measured ceilings of this box for the children too
+        if att:
+            for rr in [r["roofline"]] + list(r["kernel_rooflines"].values()):
+                if rr["unit"] == "GB/s":
+                    rr["frac_of_attainable"] = round(rr["achieved"] / att["hbm_read_gbs"], 4)
+                elif rr["bound"] == "mfma":
+                    rr["frac_of_attainable"] = round(rr["achieved"] / att["mfma_bf16_tflops"], 4)
+    out = {
+        "metric": METRIC, "value": h["pairs_per_s"], "unit": "pairs/s", "n_gpus": 1, "steps": h["steps"],
+        "warmup": h["warmup"], "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if h["config"]["act"] == "bf16" else "f32",
+        "data": "synthetic: seeded normal activations, random-init expert weights, fp32 router logits",
+        "config": {"workload": f"{head}: {DESCR[head]}", **h["config"]},
+        "roofline": h["roofline"],
+        "cpu_baseline": h["cpu_baseline"],
+        "layer_roofline": h["layer_roofline"],
+        "latency_us": h["latency_us"],
+        "kernels_us": h["kernels_us"],
+        "kernel_rooflines": h["kernel_rooflines"],
+        "n_local_pairs": h["n_local_pairs"],
+        "timed_region_s": h["timed_region_s"],
+        "attainable": att,
+        "workloads": {head: {k: v for k, v in h.items() if k not in ("workload",)}, **subs},
+    }
     print(json.dumps(out), flush=True)
 
 
