@@ -139,7 +139,8 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     permutation), plus optional rounding to multiples of `tie_quantum` to inject ties.
 
     Returns a dict of numpy arrays (bf16 tensors are uint16 bit patterns, int4 weights are
-    int32 words [e][K/8][N] with uint16 bf16 scales [e][K/gs][N]).
+    int32 words [e][K/8][N] with uint16 bf16 scales [e][K/gs][N]); the router weight W_r fp32
+    [H][E] ("w_router") and, with a Zipf bias, the fp32 bias [E] ("router_bias") come along.
     """
     T, H, E, I, el = cfg.T, cfg.H, cfg.E, cfg.I, cfg.e_local
     ss = np.random.SeedSequence(cfg.seed).spawn(2 + 3 * el + 3)
@@ -158,12 +159,14 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     else:
         out["x"] = x
     wr = _normal(s_r, (H, E), 1.0 / math.sqrt(H))
+    out["w_router"] = wr                                          # fp32 [H][E]
     logits = (x @ wr).astype(np.float32)
     if cfg.zipf_bias:
         rank = np.arange(1, E + 1, dtype=np.float64)
         if rank_perm_seed is not None:
             rank = np.random.default_rng(rank_perm_seed).permutation(rank)
-        logits += (cfg.zipf_bias * np.log(1.0 / rank)).astype(np.float32)[None, :]
+        out["router_bias"] = (cfg.zipf_bias * np.log(1.0 / rank)).astype(np.float32)
+        logits += out["router_bias"][None, :]
     if tie_quantum:
         logits = (np.rint(logits / np.float32(tie_quantum)) * np.float32(tie_quantum)).astype(np.float32)
     out["logits"] = np.ascontiguousarray(logits, dtype=np.float32)

@@ -50,6 +50,7 @@ def lib():
         L.orc_exp_ref.argtypes, L.orc_exp_ref.restype = [ctypes.c_float], ctypes.c_float
         L.orc_exp_ref_array.argtypes, L.orc_exp_ref_array.restype = [vp, vp, i64], None
         L.orc_route.argtypes, L.orc_route.restype = [vp, i32, i32, i32, vp, vp], None
+        L.orc_router_logits.argtypes, L.orc_router_logits.restype = [vp, i32, vp, vp, i32, i32, i32, vp], None
         L.orc_pack.argtypes, L.orc_pack.restype = [vp, vp, i32, i32, vp], None
         L.orc_unpack.argtypes, L.orc_unpack.restype = [vp, i32, i32, vp, vp], None
         L.orc_permute.argtypes, L.orc_permute.restype = [vp, i32, i32, i32, i32, vp, vp, vp], i32
@@ -81,6 +82,21 @@ def route(logits: np.ndarray, k: int):
     w = np.empty((T, k), np.float32)
     lib().orc_route(_p(logits), T, E, k, _p(ids), _p(w))
     return ids, w
+
+
+def router_logits(x: np.ndarray, wr: np.ndarray, bias: np.ndarray | None = None) -> np.ndarray:
+    """Router projection: fp32 logits [T][E] = fp32(sum_h x[t][h] wr[h][e]) (+ bias[e] in fp32),
+    summed in double.  x is bf16 bits (uint16) or fp32 [T][H]; wr fp32 [H][E]."""
+    act = 1 if x.dtype == np.uint16 else 0
+    x = np.ascontiguousarray(x, dtype=np.uint16 if act else np.float32)
+    wr = np.ascontiguousarray(wr, dtype=np.float32)
+    T, H = x.shape
+    E = wr.shape[1]
+    assert wr.shape[0] == H
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((T, E), np.float32)
+    lib().orc_router_logits(_p(x), act, _p(wr), _p(b), T, H, E, _p(out))
+    return out
 
 
 def pack(ids: np.ndarray, w: np.ndarray) -> np.ndarray:

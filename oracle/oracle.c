@@ -112,6 +112,35 @@ void orc_route(const float* logits, int T, int E, int k, int32_t* ids, float* w)
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Router projection ("Systems engineering playbook ...", section 1, sparse MoE: the router gate */
+/* projects each token's representation before the softmax over the experts):                  */
+/*   logits[t][e] = fp32( sum_h x[t][h] * wr[h][e] ) (+ bias[e] in fp32),                        */
+/* every product and the sum taken in double from exactly converted inputs, rounded once.       */
+/* x is bf16 (act = 1) or fp32 (act = 0) [T][H]; wr fp32 [H][E]; bias fp32 [E] or NULL.          */
+/* ------------------------------------------------------------------------------------------ */
+static double orc_bf16_bits_to_double(uint16_t b);
+
+void orc_router_logits(const void* x, int act, const float* wr, const float* bias, int T, int H, int E,
+                       float* logits) {
+  double* acc = (double*)malloc(sizeof(double) * (size_t)E);
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) acc[e] = 0.0;
+    for (int h = 0; h < H; ++h) {
+      const double xv = act ? orc_bf16_bits_to_double(((const uint16_t*)x)[(size_t)t * H + h])
+                            : (double)((const float*)x)[(size_t)t * H + h];
+      const float* row = wr + (size_t)h * E;
+      for (int e = 0; e < E; ++e) acc[e] += xv * (double)row[e];
+    }
+    for (int e = 0; e < E; ++e) {
+      float v = (float)acc[e];
+      if (bias) v = v + bias[e];
+      logits[(size_t)t * E + e] = v;
+    }
+  }
+  free(acc);
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Routing blob [2][T][k] int32: plane 0 ids, plane 1 bit pattern of the fp32 weights.         */
 /* ------------------------------------------------------------------------------------------ */
 void orc_pack(const int32_t* ids, const float* w, int T, int k, int32_t* blob) {
@@ -168,6 +197,13 @@ int orc_permute(const int32_t* blob, int T, int k, int e_first, int e_local,
 /* ------------------------------------------------------------------------------------------ */
 /* Exact conversions of stored values to double.                                               */
 /* ------------------------------------------------------------------------------------------ */
+static double orc_bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
 double orc_bf16_to_double(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;

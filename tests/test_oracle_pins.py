@@ -363,3 +363,76 @@ def test_bf16_conversion_every_pattern():
     r = ref[::97]
     fin = np.isfinite(r)
     assert np.array_equal(got[fin], r[fin])
+
+
+# ----------------------------------------------------------------------------------------------
+# Router projection: fp32(sum_h x[t][h] wr[h][e]) (+ bias in fp32), the sum exact before rounding.
+# ----------------------------------------------------------------------------------------------
+def _nearest_f32(q):
+    """Round-to-nearest-even fp32 of an exact rational (fractions.Fraction)."""
+    from fractions import Fraction
+    f = np.float32(float(q))                       # within one fp32 ulp of q
+    cands = sorted({f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))},
+                   key=lambda c: (abs(Fraction(float(c)) - q), int(np.float32(c).view(np.uint32)) & 1))
+    return cands[0]
+
+
+def test_router_logits_exact_on_small_integers():
+    """Integer inputs whose products and sums are exact in fp32: the projection is the integer
+    matrix product (checked with Python integers), for bf16 and fp32 activations, with a bias."""
+    rng = np.random.default_rng(11)
+    T, H, E = 7, 96, 13
+    xi = rng.integers(-8, 9, size=(T, H))
+    wi = rng.integers(-8, 9, size=(H, E))
+    bi = rng.integers(-100, 101, size=E)
+    exact = [[sum(int(xi[t, h]) * int(wi[h, e]) for h in range(H)) for e in range(E)] for t in range(T)]
+    x_bf16 = W.f32_to_bf16_bits(xi.astype(np.float32))
+    for x in (x_bf16, xi.astype(np.float32)):
+        got = oracle.router_logits(x, wi.astype(np.float32))
+        assert np.array_equal(got, np.array(exact, np.float32))
+        got_b = oracle.router_logits(x, wi.astype(np.float32), bi.astype(np.float32))
+        assert np.array_equal(got_b, np.array(exact, np.float32) + bi.astype(np.float32))
+
+
+def test_router_logits_dyadic_and_transposed_roles():
+    """Dyadic scales stay exact (x = i/8, w = j/32); swapping the roles of rows and columns
+    (x^T as weights, w^T as tokens) gives the transposed result."""
+    rng = np.random.default_rng(12)
+    xi = rng.integers(-16, 17, size=(5, 40))
+    wi = rng.integers(-16, 17, size=(40, 9))
+    x = (xi / 8.0).astype(np.float32)
+    w = (wi / 32.0).astype(np.float32)
+    ref = (xi @ wi).astype(np.float64) / 256.0
+    got = oracle.router_logits(x, w)
+    assert np.array_equal(got.astype(np.float64), ref)
+    got_t = oracle.router_logits(np.ascontiguousarray(w.T), np.ascontiguousarray(x.T))
+    assert np.array_equal(got_t, got.T)
+
+
+def test_router_logits_is_the_correctly_rounded_exact_sum():
+    """Random bf16 activations and fp32 weights (the recipe's distributions): each logit is the
+    round-to-nearest-even fp32 of the exact rational sum (Python fractions)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(13)
+    T, H, E = 3, 33, 6
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = (rng.standard_normal((H, E)) / np.sqrt(H)).astype(np.float32)
+    xf = W.bf16_bits_to_f32(x)
+    got = oracle.router_logits(x, w)
+    for t in range(T):
+        for e in range(E):
+            q = sum(Fraction(float(xf[t, h])) * Fraction(float(w[h, e])) for h in range(H))
+            assert got[t, e] == _nearest_f32(q), (t, e)
+
+
+def test_router_logits_near_the_recipes_fp32_logits():
+    """The input recipe computes its logits with an fp32 matrix product; the oracle's correctly
+    rounded logits lie within that product's fp32 error bound of them (|err| <= H * 2^-24 *
+    sum_h |x w| per element), so both describe the same projection."""
+    cfg = W.CONFIGS["decode"].with_(T=64, e_local=1, I=64)
+    inp = W.make_inputs(cfg)
+    got = oracle.router_logits(inp["x"], inp["w_router"]).astype(np.float64)
+    xf = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    absum = np.abs(xf) @ np.abs(inp["w_router"].astype(np.float64))
+    bound = cfg.H * 2.0 ** -24 * absum + np.spacing(np.abs(got).astype(np.float32))
+    assert np.all(np.abs(got - inp["logits"]) <= bound)
