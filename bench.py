@@ -341,6 +341,26 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
     kus = {n: float(np.mean([bev[i][j].elapsed_time(bev[i][j + 1]) * 1e3 for i in range(nb)]))
            for j, n in enumerate(names)}
 
+    # The router projection x W_r (+ bias) and routing from the hidden states (moe_route_hidden),
+    # timed apart from the step: the workloads' own steps start from the router logits.
+    from expert_grouped_gemm_softmax_amd import ops
+    wsplit = ops.prepare_router_weights(torch.from_numpy(inp["w_router"]).to(x.device))
+    rbias = torch.from_numpy(inp["router_bias"]).to(x.device) if "router_bias" in inp else None
+    r_logits = torch.empty_like(logits)
+    for _ in range(3):
+        ops.route_hidden(x, wsplit, cfg.k, bias=rbias, logits=r_logits, blob=b.blob, write_ids=False)
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)]
+    for i in range(nb):
+        rev[i][0].record(stream)
+        ops.router_logits(x, wsplit, bias=rbias, logits=r_logits)
+        rev[i][1].record(stream)
+        ops.route_packed(r_logits, cfg.k, blob=b.blob, write_ids=False)
+        rev[i][2].record(stream)
+    torch.cuda.synchronize()
+    proj_us = float(np.mean([rev[i][0].elapsed_time(rev[i][1]) * 1e3 for i in range(nb)]))
+    topk_us = float(np.mean([rev[i][1].elapsed_time(rev[i][2]) * 1e3 for i in range(nb)]))
+    del wsplit, r_logits
+
     wk = work(cfg, n_loc, nonempty)
     roof = roofline(cfg, wk["gate_up"]["flops"], wk["gate_up"]["bytes"], gu_us * 1e-6, att)
     roof.update({"kernel": "routed grouped GEMM gate/up + SwiGLU", "time_us": round(gu_us, 1),
@@ -363,6 +383,13 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
         "roofline": roof,
         "kernels_us": {n: round(v, 1) for n, v in kus.items()},
         "kernel_rooflines": kernels,
+        "router_from_hidden": {
+            "projection_us": round(proj_us, 1), "route_packed_us": round(topk_us, 1),
+            "projection_roofline": roofline(cfg, 2.0 * cfg.T * cfg.H * cfg.E,
+                                            cfg.T * cfg.H * (2 if cfg.act == "bf16" else 4) + cfg.H * cfg.E * 4
+                                            + cfg.T * cfg.E * 4, proj_us * 1e-6, att),
+            "note": "x W_r (+ bias) with W_r as two bf16 planes (2 MFMA products per weight), then "
+                    "top-k routing; not part of the step, which starts from the router logits"},
     }
     if cpu_s:
         print(f"[bench] {name}: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)

@@ -53,6 +53,9 @@ def load(path: str = LIB_PATH):
     L.moe_status_string.argtypes, L.moe_status_string.restype = [i32], ctypes.c_char_p
     L.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.moe_pack_routing.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.moe_prepare_router_weights.argtypes = [vp, i32, i32, vp, vp]
+    L.moe_router_logits.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+    L.moe_route_hidden.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.moe_route_packed.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
     L.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
@@ -63,6 +66,7 @@ def load(path: str = LIB_PATH):
     L.moe_prepare_dense_weights.argtypes = [vp, i32, i32, i32, i32, vp, vp]
     L.moe_prepare_dense_weights_f16.argtypes = [vp, i32, i32, i32, vp, vp]
     for fn in ("moe_route", "moe_pack_routing", "moe_route_packed", "moe_permute", "moe_permute_noalloc",
+               "moe_prepare_router_weights", "moe_router_logits", "moe_route_hidden",
                "moe_grouped_gemm",
                "moe_combine", "moe_prepare_dense_weights", "moe_prepare_dense_weights_f16"):
         getattr(L, fn).restype = i32

@@ -78,6 +78,46 @@ MOE_API moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w
   return enqueue([&] { return moe::launch_pack(topk_ids, topk_w, T, k, blob, as_stream(stream)); });
 }
 
+MOE_API moe_status moe_prepare_router_weights(const float* wr, int H, int E, void* out, void* stream) {
+  if (!wr || !out) return MOE_ERR_INVALID_ARG;
+  if (H < 1 || E < 1 || E > 1024 || H > (1 << 22) || !fits_i32((long long)H * E)) return MOE_ERR_INVALID_ARG;
+  return enqueue([&] { return moe::launch_prepare_router(wr, H, E, out, as_stream(stream)); });
+}
+
+namespace {
+moe_status check_router(const void* x, int x_dtype, const void* w_split, int T, int H, int E) {
+  if (!x || !w_split) return MOE_ERR_INVALID_ARG;
+  if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T < 1 || H < 1 || E < 1 || E > 1024 || H > (1 << 22)) return MOE_ERR_INVALID_ARG;
+  const long long esz = x_dtype == MOE_DT_F32 ? 4 : 2;
+  if (!fits_i32((long long)T * E) || (long long)T * H * esz >= (1LL << 31) || !fits_i32((long long)H * E))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+}  // namespace
+
+MOE_API moe_status moe_router_logits(const void* x, int x_dtype, const void* w_split, const float* bias, int T,
+                                     int H, int E, float* logits, void* stream) {
+  if (!logits) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_router(x, x_dtype, w_split, T, H, E);
+  if (st != MOE_OK) return st;
+  return enqueue([&] { return moe::launch_router_logits(x, x_dtype, w_split, bias, T, H, E, logits, as_stream(stream)); });
+}
+
+MOE_API moe_status moe_route_hidden(const void* x, int x_dtype, const void* w_split, const float* bias, int T, int H,
+                                    int E, int k, float* logits, int32_t* topk_ids, float* topk_w, int32_t* blob,
+                                    void* stream) {
+  if (!logits || !blob || (topk_ids == nullptr) != (topk_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_router(x, x_dtype, w_split, T, H, E);
+  if (st != MOE_OK) return st;
+  if (k < 1 || k > 64 || k > E || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
+  return enqueue([&] {
+    const hipError_t e = moe::launch_router_logits(x, x_dtype, w_split, bias, T, H, E, logits, as_stream(stream));
+    if (e != hipSuccess) return e;
+    return moe::launch_route(logits, T, E, k, topk_ids, topk_w, blob, as_stream(stream));
+  });
+}
+
 MOE_API size_t moe_permute_workspace_bytes(int T, int k, int e_local) {
   if (T < 1 || k < 1 || k > 64 || e_local < 1 || e_local > 1024 || !fits_i32((long long)T * k)) return 0;
   return moe::permute_workspace_bytes(T, k, e_local);

@@ -52,6 +52,9 @@ hipError_t launch_permute(const int32_t* blob, int T, int k, int e_first, int e_
                           void* workspace, hipStream_t s);
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s);
 hipError_t launch_prepare(const void* w, int E, int K, int N, int dtype, void* out, hipStream_t s);
+hipError_t launch_prepare_router(const float* w, int H, int E, void* out, hipStream_t s);
+hipError_t launch_router_logits(const void* x, int x_dtype, const void* w_split, const float* bias, int T, int H,
+                                int E, float* logits, hipStream_t s);
 hipError_t launch_combine(const void* o, int act, const int32_t* blob, const int32_t* pair_pos,
                           const void* shared, int T, int k, int H, int rows, void* y,
                           int y_dtype, hipStream_t s);

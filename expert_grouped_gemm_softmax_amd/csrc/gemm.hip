@@ -43,6 +43,7 @@ struct GemmParams {
   const void* s0;
   const void* s1;
   void* out;
+  const float* bias;   // router logits: fp32 [N] added to each output row (or NULL)
   int K, N, n_groups, rows_cap, a_rows, row_div, group_size;
 };
 
@@ -58,7 +59,8 @@ __device__ void build_tile_table(const GemmParams& p, int BM, int tiles_n, int* 
     const int e = c0 + lane;
     int tiles = 0;
     if (e < p.n_groups) {
-      int lo = p.group_offsets[e], hi = p.group_offsets[e + 1];
+      // no group offsets: one group of rows_cap identity rows (the router projection)
+      int lo = p.group_offsets ? p.group_offsets[e] : 0, hi = p.group_offsets ? p.group_offsets[e + 1] : p.rows_cap;
       lo = min(max(lo, 0), p.rows_cap);
       hi = min(max(hi, lo), p.rows_cap);
       s_goff[e] = lo;
@@ -158,10 +160,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // F16_: fp16 MFMA operands (weights scaled by 2^8); ACVT_: the activation matrix is bf16 and is
 // converted to fp16 on its way to LDS.  int4 weights always run on fp16 operands.
+// SUM_ (with GU_): the epilogue writes acc0 + acc1 (+ bias) in fp32 instead of SwiGLU: the router
+// projection over an fp32 weight split into two bf16 planes.
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1, int REGSETS_ = 2,
-          bool F16_ = Q4_, bool ACVT_ = false>
+          bool F16_ = Q4_, bool ACVT_ = false, bool SUM_ = false>
 struct Cfg {
-  static constexpr bool F16 = F16_, ACVT = ACVT_;
+  static constexpr bool F16 = F16_, ACVT = ACVT_, SUM = SUM_;
   static constexpr float OUT_MUL = F16_ ? 1.0f / kF16WeightScale : 1.0f;
   // Chunks held in registers between their loads and their LDS stores (two LDS buffers only).
   static constexpr int REGSETS = REGSETS_;
@@ -195,6 +199,7 @@ struct Cfg {
   static_assert(Q4 || BN % SLICE_ROWS == 0, "a dense piece slice stays inside one weight matrix");
   static_assert(!Q4 || F16, "int4 weights are dequantised to fp16");
   static_assert(!ACVT || F16, "activations are converted to the fp16 operand type");
+  static_assert(!SUM || (GU && !Q4 && !F16), "router sums: two dense bf16 weight planes");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
 
@@ -395,7 +400,7 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
 // loads, LDS stores and barriers whatever its NM.
 template <class C, typename OutT, int NM>
 __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* buf1, OutT* O, int N, int lane,
-                                          int wrow0, int wcol0, int row0, int rows, int n0) {
+                                          int wrow0, int wcol0, int row0, int rows, int n0, const float* bias) {
   f32x4 acc[C::NW][NM > 0 ? NM : 1][C::NTL];
 #pragma unroll
   for (int m = 0; m < C::NW; ++m)
@@ -485,8 +490,14 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < rows) {
           float v;
-          if constexpr (C::GU) v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
-          else v = acc[0][i][j][r] * C::OUT_MUL;
+          if constexpr (C::SUM) {
+            v = acc[0][i][j][r] + acc[1][i][j][r];
+            if (bias) v = v + bias[n0 + col];
+          } else if constexpr (C::GU) {
+            v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
+          } else {
+            v = acc[0][i][j][r] * C::OUT_MUL;
+          }
           store_out(O + (size_t)(row0 + row) * N + n0 + col, v);
         }
       }
@@ -494,10 +505,11 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
 
 template <class C, typename OutT, int NM>
 __device__ __forceinline__ void tile_dispatch(int nm, const TileCtx<C>& t, u16* buf0, u16* buf1, OutT* O, int N,
-                                              int lane, int wrow0, int wcol0, int row0, int rows, int n0) {
+                                              int lane, int wrow0, int wcol0, int row0, int rows, int n0,
+                                              const float* bias) {
   if constexpr (NM <= C::MT) {
-    if (nm == NM) tile_body<C, OutT, NM>(t, buf0, buf1, O, N, lane, wrow0, wcol0, row0, rows, n0);
-    else tile_dispatch<C, OutT, NM + 1>(nm, t, buf0, buf1, O, N, lane, wrow0, wcol0, row0, rows, n0);
+    if (nm == NM) tile_body<C, OutT, NM>(t, buf0, buf1, O, N, lane, wrow0, wcol0, row0, rows, n0, bias);
+    else tile_dispatch<C, OutT, NM + 1>(nm, t, buf0, buf1, O, N, lane, wrow0, wcol0, row0, rows, n0, bias);
   }
 }
 
@@ -591,7 +603,7 @@ void k_gemm_bf16(GemmParams p) {
         for (int c = 0; c < 4; ++c) t.b_dst[i][c] = lds_off_rows(m * BN + nq * 4 + (c ^ sw), kw);
       }
     }
-    tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0);
+    tile_dispatch<C, OutT, 0>(nm, t, buf0, buf1, O, p.N, lane, wrow0, wcol0, row0, rows, n0, p.bias);
   }
 }
 
@@ -883,7 +895,9 @@ __device__ __forceinline__ void dma_dispatch(int nm, const DmaCtx<C>& t, u16* sm
   }
 }
 
-template <class C, typename OutT>
+// GATHER: activation rows through row_index / row_div; false: row r of the tile reads row r of a
+// (identity rows, e.g. the shared expert), with no index loads.
+template <class C, typename OutT, bool GATHER>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD)))
 void k_gemm_dma(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
@@ -921,7 +935,7 @@ void k_gemm_dma(GemmParams p) {
     for (int j = 0; j < C::A_INST; ++j) {
       const int r = 8 * (wave + C::NWAVES * j) + (lane >> 3);
       const int rr = tc.row0 + min(r, tc.rows - 1);
-      int src = p.row_index ? p.row_index[rr] / p.row_div : rr;
+      int src = GATHER ? p.row_index[rr] / p.row_div : rr;
       src = min(max(src, 0), p.a_rows - 1);
       t.a_voff[j] = r < tc.rows ? (uint32_t)(((size_t)src * p.K + q * 8) * 2) : 0x80000000u;
     }
@@ -963,8 +977,8 @@ __device__ __forceinline__ RegTable reg_tile_table(const GemmParams& p, int BM, 
   r.lo = 0;
   r.hi = 0;
   if (lane < p.n_groups) {
-    r.lo = min(max(p.group_offsets[lane], 0), p.rows_cap);
-    r.hi = min(max(p.group_offsets[lane + 1], r.lo), p.rows_cap);
+    r.lo = min(max(p.group_offsets ? p.group_offsets[lane] : 0, 0), p.rows_cap);
+    r.hi = min(max(p.group_offsets ? p.group_offsets[lane + 1] : p.rows_cap, r.lo), p.rows_cap);
     tiles = ((r.hi - r.lo + BM - 1) / BM) * tiles_n;
   }
   const int incl = wave_scan_incl(tiles);
@@ -1167,7 +1181,10 @@ hipError_t run_dma(const GemmParams& p, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  k_gemm_dma<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
+  if (p.row_index)
+    k_gemm_dma<C, OutT, true><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
+  else
+    k_gemm_dma<C, OutT, false><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
   return hipGetLastError();
 }
 
@@ -1275,7 +1292,7 @@ hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  if constexpr (C::STAGES == 1 && !C::Q4) {
+  if constexpr (C::STAGES == 1 && !C::Q4 && !C::SUM) {
     if (p.row_index == nullptr && (p.K / C::KC) % 2 == 0) {
       k_gemm_stream<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
       return hipGetLastError();
@@ -1376,7 +1393,7 @@ hipError_t run_dma_dn(const GemmParams& p, hipStream_t s) {
 hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   GemmParams p;
   p.a = a.a; p.row_index = a.row_index; p.group_offsets = a.group_offsets;
-  p.w0 = a.w0; p.w1 = a.w1; p.s0 = a.s0; p.s1 = a.s1; p.out = a.out;
+  p.w0 = a.w0; p.w1 = a.w1; p.s0 = a.s0; p.s1 = a.s1; p.out = a.out; p.bias = nullptr;
   p.K = a.K; p.N = a.N; p.n_groups = a.n_groups; p.rows_cap = a.rows_cap; p.a_rows = a.a_rows;
   p.row_div = a.row_div; p.group_size = a.group_size > 0 ? a.group_size : a.K;
   const bool gu = a.op == MOE_OP_GATE_UP_SWIGLU;
@@ -1410,6 +1427,54 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f16, f32out, s);
   if (f16) return f32out ? run_dma_dn<true, float>(p, s) : run_dma_dn<true, _Float16>(p, s);
   return f32out ? run_dma_dn<false, float>(p, s) : run_dma_dn<false, u16>(p, s);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Router projection: logits = x W_r (+ bias), W_r held as two bf16 planes W_hi + W_lo
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+// fp32 path (fp32 activations, or E not a multiple of 64): one thread per (token, expert), the
+// K sum in order with fma; W_hi + W_lo is exact in fp32.
+__global__ __launch_bounds__(256) void k_router_f32(const void* __restrict__ x, int x_bf16, const u16* __restrict__ w,
+                                                    const float* __restrict__ bias, int T, int H, int E,
+                                                    float* __restrict__ logits) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)T * E) return;
+  const int t = (int)(i / E), e = (int)(i % E);
+  const u16* hi = w + (size_t)e * H;
+  const u16* lo = w + ((size_t)E + e) * H;
+  float acc = 0.0f;
+  for (int h = 0; h < H; ++h) {
+    const float xv = x_bf16 ? bf16_to_f32(static_cast<const u16*>(x)[(size_t)t * H + h])
+                            : static_cast<const float*>(x)[(size_t)t * H + h];
+    acc = fmaf(xv, bf16_to_f32(hi[h]) + bf16_to_f32(lo[h]), acc);
+  }
+  if (bias) acc = acc + bias[e];
+  logits[i] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const void* x, int x_dtype, const void* w_split, const float* bias, int T, int H,
+                                int E, float* logits, hipStream_t s) {
+  if (x_dtype != MOE_DT_BF16 || E % 64 != 0 || H % 64 != 0) {
+    const long long n = (long long)T * E;
+    k_router_f32<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(x, x_dtype == MOE_DT_BF16, static_cast<const u16*>(w_split),
+                                                                   bias, T, H, E, logits);
+    return hipGetLastError();
+  }
+  GemmParams p;
+  p.a = x; p.row_index = nullptr; p.group_offsets = nullptr;    // one group of T identity rows
+  p.w0 = w_split; p.w1 = static_cast<const u16*>(w_split) + (size_t)E * H;
+  p.s0 = p.s1 = nullptr; p.out = logits; p.bias = bias;
+  p.K = H; p.N = E; p.n_groups = 1; p.rows_cap = T; p.a_rows = T; p.row_div = 1; p.group_size = H;
+  // 256-row tiles (64 experts wide) when they give every compute unit about one tile, else
+  // 32-row tiles, four workgroups per compute unit
+  const long long big_tiles = (long long)((T + 255) / 256) * (E / 64);
+  if (2 * big_tiles >= device_cu_count())
+    return run_bf16<Cfg<256, 64, 4, 1, 2, true, false, 1, 2, false, false, true>, float>(p, 1, s);
+  return run_bf16<Cfg<32, 64, 1, 4, 1, true, false, 4, 2, false, false, true>, float>(p, 4, s);
 }
 
 }  // namespace moe

@@ -40,7 +40,35 @@ __global__ __launch_bounds__(256) void k_prepare(const T* __restrict__ w, int K,
   }
 }
 
+// Router weights: W_r fp32 [H][E] -> two bf16 planes [2][E][H] (hi = bf16(W), lo = bf16(W - hi)),
+// each expert's H weights contiguous.  hi + lo keeps 16 significant bits of W: |W - hi - lo| <=
+// 2^-18 |W|, and W - hi is exact in fp32.
+__global__ __launch_bounds__(256) void k_prepare_router(const float* __restrict__ w, int H, int E, u16* __restrict__ out) {
+  __shared__ float tile[64][64 + 1];
+  const int h0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int h = h0 + r, e = e0 + tx;
+    if (h < H && e < E) tile[r][tx] = w[(size_t)h * E + e];
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int e = e0 + r, h = h0 + tx;
+    if (e < E && h < H) {
+      const float v = tile[tx][r];
+      const u16 hi = f32_to_bf16(v);
+      out[(size_t)e * H + h] = hi;
+      out[((size_t)E + e) * H + h] = f32_to_bf16(v - bf16_to_f32(hi));
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prepare_router(const float* w, int H, int E, void* out, hipStream_t s) {
+  k_prepare_router<<<dim3((E + 63) / 64, (H + 63) / 64), dim3(256), 0, s>>>(w, H, E, static_cast<u16*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_prepare(const void* w, int E, int K, int N, int dtype, void* out, hipStream_t s) {
   const dim3 grid((N + 63) / 64, (K + 63) / 64, E), block(256);

@@ -108,12 +108,13 @@ class MoELayer:
         self.e_first, self.e_local = e_first, e_local
         self.weights = weights
         self.act_dtype = act_dtype
-        # Expert outputs and the layer output are fp32: each is a partial sum (over a token's
-        # experts here, over devices in an expert-parallel reduce-scatter) and a bf16 rounding of
-        # every row would add an error proportional to |y| on top of the bf16 GEMM operands.
-        self.o_dtype = torch.float32
+        # The layer output is fp32 (a partial sum, over devices in an expert-parallel
+        # reduce-scatter).  Expert output rows take h's dtype when that is fp16 (its 2^-12 rounding
+        # is small beside the bar, and the combine reads half the bytes; it accumulates in fp32),
+        # else fp32: a bf16 rounding of every row would add an error proportional to |y|.
         self.y_dtype = y_dtype
         self.h_dtype = weights.h_dtype if act_dtype == torch.bfloat16 else act_dtype
+        self.o_dtype = torch.float16 if self.h_dtype == torch.float16 else torch.float32
         self.shared_I = 0 if weights.shared_gate is None else weights.shared_gate.shape[0]
         self._check_shapes()
         self._buf: dict[int, Buffers] = {}

@@ -75,6 +75,48 @@ def route_packed(logits: torch.Tensor, k: int, ids: torch.Tensor | None = None, 
     return ids, w, blob
 
 
+def prepare_router_weights(wr: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Router weight W_r fp32 [H][E] -> bf16 [2][E][H] (hi, lo planes) for router_logits."""
+    H, E = wr.shape
+    assert wr.dtype == torch.float32 and wr.is_contiguous()
+    out = out if out is not None else torch.empty((2, E, H), dtype=torch.bfloat16, device=wr.device)
+    _dev(wr, out)
+    check("moe_prepare_router_weights", load().moe_prepare_router_weights(_ptr(wr), H, E, _ptr(out), _stream(stream)))
+    return out
+
+
+def router_logits(x: torch.Tensor, w_split: torch.Tensor, bias: torch.Tensor | None = None,
+                  logits: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """x [T][H] (bf16 or fp32) -> fp32 logits [T][E] = x W_r (+ bias)."""
+    T, H = x.shape
+    E = w_split.shape[1]
+    assert w_split.shape == (2, E, H) and w_split.dtype == torch.bfloat16
+    logits = logits if logits is not None else torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _dev(x, w_split, bias, logits)
+    check("moe_router_logits", load().moe_router_logits(_ptr(x), _DT[x.dtype], _ptr(w_split), _ptr(bias), T, H, E,
+                                                        _ptr(logits), _stream(stream)))
+    return logits
+
+
+def route_hidden(x: torch.Tensor, w_split: torch.Tensor, k: int, bias: torch.Tensor | None = None,
+                 logits=None, ids=None, w=None, blob=None, write_ids: bool = True, stream=None):
+    """Router projection then route_packed -> (logits, ids, w, blob)."""
+    T, H = x.shape
+    E = w_split.shape[1]
+    dev = x.device
+    logits = logits if logits is not None else torch.empty((T, E), dtype=torch.float32, device=dev)
+    if write_ids:
+        ids = ids if ids is not None else torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = w if w is not None else torch.empty((T, k), dtype=torch.float32, device=dev)
+    else:
+        ids = w = None
+    blob = blob if blob is not None else torch.empty((2, T, k), dtype=torch.int32, device=dev)
+    _dev(x, w_split, bias, logits, ids, w, blob)
+    check("moe_route_hidden", load().moe_route_hidden(_ptr(x), _DT[x.dtype], _ptr(w_split), _ptr(bias), T, H, E, k,
+                                                      _ptr(logits), _ptr(ids), _ptr(w), _ptr(blob), _stream(stream)))
+    return logits, ids, w, blob
+
+
 def permute_workspace_bytes(T: int, k: int, e_local: int) -> int:
     return int(load().moe_permute_workspace_bytes(T, k, e_local))
 

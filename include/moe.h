@@ -10,8 +10,10 @@
  *   4. moe_grouped_gemm  per-expert SwiGLU FFN: fused gate/up projection + SwiGLU, then the down
  *                        projection, with bf16 or symmetric int4 group-quantised (W4A16) weights;
  *   5. moe_combine       weighted sum of each token's expert outputs back in token order.
- * Also: moe_route_packed (steps 1 and 2 in one launch) and moe_prepare_dense_weights (one-time,
- * load-time storage of dense expert weights in the layout the bf16 grouped GEMM reads).
+ * Also: moe_route_packed (steps 1 and 2 in one launch); moe_router_logits and moe_route_hidden
+ * (the router projection x W_r before step 1, and with steps 1-2 after it); moe_permute_noalloc
+ * (step 3 without a workspace); one-time, load-time weight preparation (moe_prepare_dense_weights,
+ * moe_prepare_dense_weights_f16, moe_prepare_router_weights).
  *
  * Conventions shared by every entry point:
  *   - Every array argument is a DEVICE pointer owned by the caller.  The library never allocates,
@@ -104,6 +106,41 @@ const char* moe_status_string(int status);
  */
 moe_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
                      void* stream);
+
+/*
+ * moe_prepare_router_weights -- one-time preparation of the router weight for the projections
+ * below: W_r fp32 [H][E] (logits = x W_r) -> two bf16 planes out [2][E][H], hi = bf16(W_r) and
+ * lo = bf16(W_r - hi), each expert's H weights contiguous.  hi + lo keeps 16 significant bits of
+ * every weight (|W_r - hi - lo| <= 2^-18 |W_r|).  wr and out must not overlap.
+ *   Limits: 1 <= E <= 1024, 1 <= H <= 2^22, H * E < 2^31.
+ */
+moe_status moe_prepare_router_weights(const float* wr, int H, int E, void* out, void* stream);
+
+/*
+ * moe_router_logits -- the router projection ("Systems engineering playbook ...", section 1,
+ * sparse MoE: the router gate projects each token's representation before the softmax over the
+ * experts): logits[t][e] = sum_h x[t][h] (hi[e][h] + lo[e][h]) (+ bias[e]) in fp32.
+ *   x        [T][H] bf16 (MOE_DT_BF16) or fp32 (MOE_DT_F32), row-major.
+ *   w_split  bf16 [2][E][H] from moe_prepare_router_weights.
+ *   bias     fp32 [E] added to every token's logits, or NULL.
+ *   logits   fp32 [T][E] out.
+ * bf16 x with H and E multiples of 64 runs on bf16 MFMA (each product x * hi and x * lo exact,
+ * fp32 accumulation in a fixed order); otherwise an fp32 vector loop over h in order.  Against
+ * the exact sum with W_r the error is at most (2^-18 + n_acc 2^-24) * sum_h |x[t][h] W_r[h][e]|
+ * with n_acc = H + 2 (fp32 path) or H / 32 + 34 (MFMA path), plus the rounding of the bias addition.
+ *   Limits: 1 <= T, 1 <= H <= 2^22, 1 <= E <= 1024, T * H * sizeof(x) < 2^31, T * E < 2^31.
+ */
+moe_status moe_router_logits(const void* x, int x_dtype, const void* w_split, const float* bias, int T, int H,
+                             int E, float* logits, void* stream);
+
+/*
+ * moe_route_hidden -- the router projection followed by moe_route_packed, from the hidden states:
+ * logits (written to `logits`, fp32 [T][E]) then ids, weights and blob exactly as moe_route_packed
+ * computes them from those logits.  topk_ids / topk_w: both written, or both NULL.
+ *   Limits: those of moe_router_logits and moe_route_packed.
+ */
+moe_status moe_route_hidden(const void* x, int x_dtype, const void* w_split, const float* bias, int T, int H, int E,
+                            int k, float* logits, int32_t* topk_ids, float* topk_w, int32_t* blob, void* stream);
 
 /*
  * moe_pack_routing -- routing blob ("Systems engineering playbook ...", section 3, 3-to-2

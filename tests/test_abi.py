@@ -220,3 +220,28 @@ def test_calibration_library_exports_and_rejects_bad_sizes():
     assert lib.moe_calib_read(None, unit, 8, FAKE, None) == HIP_INVALID
     assert lib.moe_calib_read(FAKE, unit + 16, 8, FAKE, None) == HIP_INVALID
     assert lib.moe_calib_read(FAKE, unit, 8, None, None) == HIP_INVALID
+
+
+def test_router_entry_points_validation(L):
+    F = FAKE
+    # moe_prepare_router_weights(wr, H, E, out, stream)
+    assert L.moe_prepare_router_weights(None, 64, 8, F, None) == INV
+    assert L.moe_prepare_router_weights(F, 64, 8, None, None) == INV
+    assert L.moe_prepare_router_weights(F, 0, 8, F, None) == INV
+    assert L.moe_prepare_router_weights(F, 64, 0, F, None) == INV
+    assert L.moe_prepare_router_weights(F, 64, 1025, F, None) == INV
+    # moe_router_logits(x, x_dtype, w_split, bias, T, H, E, logits, stream)
+    assert L.moe_router_logits(None, 1, F, None, 8, 64, 16, F, None) == INV
+    assert L.moe_router_logits(F, 1, None, None, 8, 64, 16, F, None) == INV
+    assert L.moe_router_logits(F, 1, F, None, 8, 64, 16, None, None) == INV
+    assert L.moe_router_logits(F, 2, F, None, 8, 64, 16, F, None) == UNS       # fp16 x
+    assert L.moe_router_logits(F, 1, F, None, 0, 64, 16, F, None) == INV
+    assert L.moe_router_logits(F, 1, F, None, 8, 64, 1025, F, None) == INV
+    assert L.moe_router_logits(F, 1, F, None, 1 << 20, 1 << 12, 16, F, None) == INV   # x bytes >= 2^31
+    # moe_route_hidden(x, x_dtype, w_split, bias, T, H, E, k, logits, ids, w, blob, stream)
+    assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 2, None, F, F, F, None) == INV
+    assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 2, F, F, F, None, None) == INV
+    assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 2, F, None, F, F, None) == INV
+    assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 0, F, F, F, F, None) == INV
+    assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 17, F, F, F, F, None) == INV
+    assert L.moe_route_hidden(F, 0, F, None, 8, 64, 1025, 2, F, F, F, F, None) == INV

@@ -315,21 +315,26 @@ def test_down_projection_16bit_output_and_16bit_combine(name, h_dtype, hint):
     b = layer.buffers(cfg.T, x.device)
     assert b.h.dtype == h_dtype
     Wt = layer.weights
-    o16 = torch.empty(b.o.shape, dtype=h_dtype, device=x.device)
-    ops.grouped_gemm(1, b.h, b.group_offsets, Wt.w_down, None, o16, K=cfg.I, N=cfg.H, s0=Wt.s_down,
-                     group_size=Wt.group_size, m_hint=hint)
-    sh16 = None
+    def down(out_dtype, shared=False):
+        if shared:
+            out = torch.empty(b.shared_o.shape, dtype=out_dtype, device=x.device)
+            return ops.grouped_gemm(1, b.shared_h, b.shared_offsets, Wt.shared_down, None, out, K=cfg.shared_I,
+                                    N=cfg.H, m_hint=cfg.T)
+        out = torch.empty(b.o.shape, dtype=out_dtype, device=x.device)
+        return ops.grouped_gemm(1, b.h, b.group_offsets, Wt.w_down, None, out, K=cfg.I, N=cfg.H, s0=Wt.s_down,
+                                group_size=Wt.group_size, m_hint=hint)
+
+    o16, o32 = down(h_dtype), down(torch.float32)
+    sh16 = sh32 = None
     if cfg.shared_I:
-        sh16 = torch.empty(b.shared_o.shape, dtype=h_dtype, device=x.device)
-        ops.grouped_gemm(1, b.shared_h, b.shared_offsets, Wt.shared_down, None, sh16, K=cfg.shared_I, N=cfg.H,
-                         m_hint=cfg.T)
+        sh16, sh32 = down(h_dtype, shared=True), down(torch.float32, shared=True)
     y = ops.combine(o16, b.blob, b.pair_pos, sh16, y_dtype=torch.float32)
     torch.cuda.synchronize()
     n = int(b.group_offsets[-1])
     bits = torch.int16
-    assert torch.equal(o16[:n].view(bits), b.o[:n].to(h_dtype).view(bits))
+    assert torch.equal(o16[:n].view(bits), o32[:n].to(h_dtype).view(bits))
     if sh16 is not None:
-        assert torch.equal(sh16.view(bits), b.shared_o.to(h_dtype).view(bits))
+        assert torch.equal(sh16.view(bits), sh32.to(h_dtype).view(bits))
     ids, w = oracle.route(inp["logits"], cfg.k)
     ref = oracle.layer(inp, cfg, ids, w, threads=8)
     _check_close(_np(y).astype(np.float64), ref, f"{name} h {h_dtype} 16-bit o")
@@ -452,3 +457,65 @@ def test_layer_at_the_largest_activation_matrix(max_rows_inputs, variant):
     _check_close(yn, ref, f"max_rows/{variant}")
     del layer, b, y
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------------------------
+# Router projection on the GPU (logits = x W_r (+ bias)) before routing
+# ----------------------------------------------------------------------------------------------
+def _router_case(cfg):
+    c = cfg.with_(e_local=1, I=64, shared_I=0, wfmt="dense")     # router inputs only
+    inp = W.make_inputs(c)
+    x = _upload_x(inp, cfg)
+    wr = torch.from_numpy(inp["w_router"]).to(_dev())
+    bias = torch.from_numpy(inp["router_bias"]).to(_dev()) if "router_bias" in inp else None
+    return inp, x, wr, bias
+
+
+def _upload_x(inp, cfg):
+    if cfg.act == "bf16":
+        return torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(_dev())
+    return torch.from_numpy(inp["x"]).to(_dev())
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_router_projection_and_routing_from_hidden_states(name):
+    """moe_route_hidden on every workload: each logit within the derived error bound of the
+    oracle's fp64 projection, routing on the GPU's logits bit-exact against the oracle routing the
+    same logits, top-k ids equal to the oracle's wherever the bound decides them, and weights
+    within the error budget that follows from the logits' bound."""
+    cfg = W.CONFIGS[name]
+    inp, x, wr, bias = _router_case(cfg)
+    wsplit = ops.prepare_router_weights(wr)
+    logits, ids, w, blob = ops.route_hidden(x, wsplit, cfg.k, bias=bias)
+    torch.cuda.synchronize()
+    g_logits, g_ids, g_w = _np(logits), _np(ids), _np(w)
+    # the projection against the oracle, element by element
+    ref = oracle.router_logits(inp["x"], inp["w_router"], inp.get("router_bias"))
+    xf = W.bf16_bits_to_f32(inp["x"]) if cfg.act == "bf16" else inp["x"]
+    absum = np.abs(xf.astype(np.float64)) @ np.abs(inp["w_router"].astype(np.float64))
+    # the bound moe.h states: rounding steps of the fp32 sums (MFMA path: one per 32-product step
+    # and up to 32 inside a step, plus the sum of the two planes; fp32 path: one per product)
+    mfma = cfg.act == "bf16" and cfg.H % 64 == 0 and cfg.E % 64 == 0
+    n_acc = (cfg.H // 32 + 32 + 2) if mfma else (cfg.H + 2)
+    bound = (2.0 ** -18 + n_acc * 2.0 ** -24) * absum + 2 * np.spacing(np.abs(ref).astype(np.float32))
+    err = np.abs(g_logits.astype(np.float64) - ref)
+    print(f"{name}: max |logit err| {err.max():.3e}, max err/bound {np.max(err / bound):.3f}")
+    assert np.all(err <= bound)
+    # routing of the GPU's own logits: bit-exact (the logits-in path)
+    r_ids, r_w = oracle.route(g_logits, cfg.k)
+    assert np.array_equal(g_ids, r_ids) and np.array_equal(g_w.view(np.int32), r_w.view(np.int32))
+    assert np.array_equal(_np(blob), oracle.pack(r_ids, r_w))
+    # against the oracle's own logits: ids where decidable, weights within the budget
+    o_ids, o_w = oracle.route(ref, cfg.k)
+    T, k = o_ids.shape
+    srt = -np.sort(-ref.astype(np.float64), axis=1)
+    bmax = bound.max(axis=1)
+    gap_ok = (srt[:, k - 1] - srt[:, k] > 2 * bmax) if cfg.E > k else np.ones(T, bool)
+    same_set = np.array([set(a) == set(b) for a, b in zip(g_ids, o_ids)])
+    assert np.all(same_set[gap_ok])
+    order_ok = gap_ok & np.all(srt[:, :k - 1] - srt[:, 1:k] > 2 * bmax[:, None], axis=1)
+    assert np.array_equal(g_ids[order_ok], o_ids[order_ok])
+    budget = 4 * bmax[:, None] * o_w + 8 * np.spacing(o_w)
+    assert np.all(np.abs(g_w[order_ok].astype(np.float64) - o_w[order_ok]) <= budget[order_ok])
+    print(f"{name}: decided sets {gap_ok.mean():.4f}, decided order {order_ok.mean():.4f}, "
+          f"sets equal overall {same_set.mean():.4f}")
