@@ -23,7 +23,8 @@ import numpy as np
 
 __all__ = [
     "MoEConfig", "CONFIGS", "make_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "quantize_int4_sym", "pack_int4", "expected_rows_per_group", "rows_capacity",
+    "quantize_int4_sym", "pack_int4", "quantize_fp8_e4m3_channel", "expected_rows_per_group",
+    "rows_capacity",
 ]
 
 
@@ -40,7 +41,7 @@ class MoEConfig:
     e_first: int
     e_local: int
     act: str = "bf16"          # "f32" or "bf16": activations and dense weights
-    wfmt: str = "dense"        # "dense" or "int4"
+    wfmt: str = "dense"        # "dense", "int4" or "fp8" (OCP e4m3, one scale per output channel)
     group_size: int = 128      # int4 quantisation group along K
     shared_I: int = 0          # intermediate size of the always-on shared expert (0: none)
     zipf_bias: float = 0.0     # additive logit bias zipf_bias * ln(1 / (e + 1)) per expert
@@ -63,6 +64,11 @@ CONFIGS = {
     # Prefill shapes with symmetric int4 expert weights, groups of 128 along K, bf16 scales.
     "w4a16": MoEConfig("w4a16", T=8192, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
                        wfmt="int4", group_size=128),
+    # Decode and prefill shapes with FP8 (e4m3) expert weights, one bf16 scale per output channel.
+    "fp8_decode": MoEConfig("fp8_decode", T=512, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
+                            wfmt="fp8"),
+    "fp8_prefill": MoEConfig("fp8_prefill", T=8192, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
+                             wfmt="fp8"),
 }
 
 
@@ -107,6 +113,25 @@ def quantize_int4_sym(w: np.ndarray, group_size: int):
     return q, s_bits
 
 
+FP8_E4M3_MAX = 448.0
+
+
+def quantize_fp8_e4m3_channel(w: np.ndarray):
+    """FP8 (OCP e4m3) quantiser for test weights w[K][N] (fp32), one scale per output channel n:
+    s = bf16(max_k |w[k][n]| / 448), q = e4m3(clamp(w / s, -448, 448)) rounded to nearest even; an
+    all-zero column gets s = 0, q = 0.  Returns (q uint8 [N][K] -- output channel major, each
+    column's K bytes contiguous -- and scale bits uint16 [N])."""
+    import torch
+    amax = np.abs(w).max(axis=0)                                  # [N]
+    s_bits = f32_to_bf16_bits((amax / np.float32(FP8_E4M3_MAX)).astype(np.float32))
+    s = bf16_bits_to_f32(s_bits)
+    safe = np.where(s == 0, np.float32(1.0), s)
+    r = np.clip(w / safe[None, :], -FP8_E4M3_MAX, FP8_E4M3_MAX).astype(np.float32)
+    r = np.where(s[None, :] == 0, np.float32(0.0), r)
+    q = torch.from_numpy(np.ascontiguousarray(r.T)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(q), s_bits
+
+
 def pack_int4(q: np.ndarray) -> np.ndarray:
     """Pack int4 values q[K][N] (in [-8, 7]) into int32 words [K/8][N]: the two's-complement
     nibble at bits 4i..4i+3 of word [kb][n] holds q[8*kb + i][n]."""
@@ -139,7 +164,8 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     permutation), plus optional rounding to multiples of `tie_quantum` to inject ties.
 
     Returns a dict of numpy arrays (bf16 tensors are uint16 bit patterns, int4 weights are
-    int32 words [e][K/8][N] with uint16 bf16 scales [e][K/gs][N]); the router weight W_r fp32
+    int32 words [e][K/8][N] with uint16 bf16 scales [e][K/gs][N], fp8 weights e4m3 bytes
+    [e][N][K] with uint16 bf16 scales [e][N]); the router weight W_r fp32
     [H][E] ("w_router") and, with a Zipf bias, the fp32 bias [E] ("router_bias") come along.
     """
     T, H, E, I, el = cfg.T, cfg.H, cfg.E, cfg.I, cfg.e_local
@@ -148,8 +174,8 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     s_g, s_u, s_d = ss[2:2 + el], ss[2 + el:2 + 2 * el], ss[2 + 2 * el:2 + 3 * el]
     s_sh = ss[2 + 3 * el:]
     bf16 = cfg.act == "bf16"
-    assert cfg.act in ("f32", "bf16") and cfg.wfmt in ("dense", "int4")
-    assert not (cfg.wfmt == "int4" and not bf16), "int4 weights need bf16 activations"
+    assert cfg.act in ("f32", "bf16") and cfg.wfmt in ("dense", "int4", "fp8")
+    assert cfg.wfmt == "dense" or bf16, "quantised weights need bf16 activations"
 
     out: dict = {}
     x = _normal(s_x, (T, H), 1.0)
@@ -177,6 +203,8 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
         if cfg.wfmt == "int4":
             q, s_bits = quantize_int4_sym(w, cfg.group_size)
             return pack_int4(q), s_bits
+        if cfg.wfmt == "fp8":
+            return quantize_fp8_e4m3_channel(w)
         return f32_to_bf16_bits(w) if bf16 else w
 
     jobs = ([(s, (H, I), H) for s in s_g] + [(s, (H, I), H) for s in s_u] +
@@ -186,7 +214,7 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
     names = ("w_gate", "w_up", "w_down")
     for m, name in enumerate(names):
         part = res[m * el:(m + 1) * el]
-        if cfg.wfmt == "int4":
+        if cfg.wfmt in ("int4", "fp8"):
             out[name] = np.stack([p[0] for p in part])
             out[name + "_scale"] = np.stack([p[1] for p in part])
         else:

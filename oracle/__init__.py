@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16 = 0, 1
-DENSE, INT4 = 0, 1
+DENSE, INT4, FP8 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -56,6 +56,7 @@ def lib():
         L.orc_permute.argtypes, L.orc_permute.restype = [vp, i32, i32, i32, i32, vp, vp, vp], i32
         L.orc_bf16_to_double.argtypes, L.orc_bf16_to_double.restype = [ctypes.c_uint16], ctypes.c_double
         L.orc_int4_nibble.argtypes, L.orc_int4_nibble.restype = [ctypes.c_int32, i32], i32
+        L.orc_fp8_e4m3_to_double.argtypes, L.orc_fp8_e4m3_to_double.restype = [ctypes.c_uint8], ctypes.c_double
         L.orc_expand_matrix.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
         L.orc_expand_matrix.restype = None
         L.orc_layer.argtypes, L.orc_layer.restype = [ctypes.POINTER(_LayerArgs), vp, i32, vp], None
@@ -132,6 +133,10 @@ def bf16_to_double(b: int) -> float:
     return lib().orc_bf16_to_double(int(b))
 
 
+def fp8_e4m3_to_double(code: int) -> float:
+    return lib().orc_fp8_e4m3_to_double(int(code) & 0xFF)
+
+
 def int4_nibble(word: int, i: int) -> int:
     return lib().orc_int4_nibble(ctypes.c_int32(int(np.int32(np.uint32(word & 0xFFFFFFFF)))).value, i)
 
@@ -157,7 +162,7 @@ def layer(inputs: dict, cfg, ids: np.ndarray, w: np.ndarray, tokens=None, thread
     a.T, a.H, a.I, a.k = T, H, cfg.I, cfg.k
     a.e_first, a.e_local = cfg.e_first, cfg.e_local
     a.act = BF16 if cfg.act == "bf16" else F32
-    a.wfmt = INT4 if cfg.wfmt == "int4" else DENSE
+    a.wfmt = {"int4": INT4, "fp8": FP8}.get(cfg.wfmt, DENSE)
     a.group_size = cfg.group_size
     a.shared_I = cfg.shared_I
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -168,7 +173,7 @@ def layer(inputs: dict, cfg, ids: np.ndarray, w: np.ndarray, tokens=None, thread
         arr = np.ascontiguousarray(inputs[name])
         keep.append(arr)
         setattr(a, f, _p(arr))
-    if cfg.wfmt == "int4":
+    if cfg.wfmt in ("int4", "fp8"):
         for f, name in (("sg", "w_gate_scale"), ("su", "w_up_scale"), ("sd", "w_down_scale")):
             arr = np.ascontiguousarray(inputs[name], dtype=np.uint16)
             keep.append(arr)

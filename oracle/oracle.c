@@ -217,19 +217,38 @@ int orc_int4_nibble(int32_t word, int i) {
   return v >= 8 ? v - 16 : v;
 }
 
+/* OCP FP8 E4M3 ("FN": no infinities) byte -> exact value: sign bit 7, exponent bits 3..6 with
+ * bias 7, mantissa bits 0..2; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN.  The
+ * FP8-served models of "vLLM TPU Inference v0.31.0" (inter-chip transfer split) carry their
+ * weights in 8-bit floating point; this reading takes OCP E4M3 with one scale per output
+ * channel. */
+double orc_fp8_e4m3_to_double(uint8_t c) {
+  const int e = (c >> 3) & 0xF, m = c & 7;
+  const double sign = (c & 0x80) ? -1.0 : 1.0;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) return sign * ldexp((double)m / 8.0, -6);
+  return sign * ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
-enum { ORC_DENSE = 0, ORC_INT4 = 1 };
+enum { ORC_DENSE = 0, ORC_INT4 = 1, ORC_FP8 = 2 };
 
 /* Row kk of matrix `e` of a stack of [K][N] matrices, converted exactly to double. */
 typedef struct {
-  const void* w;            /* dense: f32/bf16 [E][K][N]; int4: int32 words [E][K/8][N] */
-  const uint16_t* scale;    /* int4 only: bf16 [E][K/gs][N] */
+  const void* w;            /* dense: f32/bf16 [E][K][N]; int4: int32 words [E][K/8][N];
+                               fp8: e4m3 bytes [E][N][K] (output channel major) */
+  const uint16_t* scale;    /* int4: bf16 [E][K/gs][N]; fp8: bf16 [E][N] per output channel */
   int fmt, act, K, N, gs;
 } orc_mat;
 
 static void orc_row(const orc_mat* m, int e, int kk, double* out) {
   const size_t N = (size_t)m->N;
-  if (m->fmt == ORC_INT4) {
+  if (m->fmt == ORC_FP8) {
+    const uint8_t* q = (const uint8_t*)m->w + (size_t)e * N * m->K;
+    const uint16_t* s = m->scale + (size_t)e * N;
+    for (size_t n = 0; n < N; ++n)
+      out[n] = orc_fp8_e4m3_to_double(q[n * (size_t)m->K + kk]) * orc_bf16_to_double(s[n]);
+  } else if (m->fmt == ORC_INT4) {
     const int32_t* words = (const int32_t*)m->w + ((size_t)e * (m->K / 8) + kk / 8) * N;
     const uint16_t* s = m->scale + ((size_t)e * (m->K / m->gs) + kk / m->gs) * N;
     for (size_t n = 0; n < N; ++n)
@@ -273,7 +292,7 @@ static void orc_swiglu(const double* a, const orc_mat* g, const orc_mat* u, cons
 typedef struct {
   int T, H, I, k, e_first, e_local;
   int act;          /* ORC_F32 or ORC_BF16: x, dense weights, shared weights */
-  int wfmt;         /* ORC_DENSE or ORC_INT4 for the routed experts */
+  int wfmt;         /* ORC_DENSE, ORC_INT4 or ORC_FP8 for the routed experts */
   int group_size;   /* int4 group along K */
   int shared_I;     /* 0: no shared expert */
   const void* x;    /* [T][H] */

@@ -436,3 +436,59 @@ def test_router_logits_near_the_recipes_fp32_logits():
     absum = np.abs(xf) @ np.abs(inp["w_router"].astype(np.float64))
     bound = cfg.H * 2.0 ** -24 * absum + np.spacing(np.abs(got).astype(np.float32))
     assert np.all(np.abs(got - inp["logits"]) <= bound)
+
+
+# ----------------------------------------------------------------------------------------------
+# FP8 (OCP e4m3) weights: exact decode of every code; per-channel scales; the layer with fp8
+# weights equals the layer with the same weights decoded and given as fp32 dense weights.
+# ----------------------------------------------------------------------------------------------
+def test_fp8_e4m3_decode_every_code():
+    """All 256 codes against torch's float8_e4m3fn (a library decode of the same format), plus
+    values worked by hand from the format: sign, 4-bit exponent with bias 7, 3-bit mantissa."""
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8_e4m3_to_double(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    hand = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3c: 1.5, 0x7e: 448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+            0x08: 2.0 ** -6, 0xb8: -1.0, 0xfe: -448.0}
+    for c, v in hand.items():
+        assert oracle.fp8_e4m3_to_double(c) == v, hex(c)
+    assert math.isnan(oracle.fp8_e4m3_to_double(0x7f)) and math.isnan(oracle.fp8_e4m3_to_double(0xff))
+    assert math.copysign(1.0, oracle.fp8_e4m3_to_double(0x80)) == -1.0
+
+
+def test_fp8_matrix_expansion_by_hand():
+    """A 2 x 3 matrix written by hand as fp8 bytes [N][K] with one bf16 scale per column n."""
+    q = np.array([[0x38, 0x40], [0xb8, 0x00], [0x3c, 0x7e]], np.uint8)[None]     # [1][N=3][K=2]
+    s = W.f32_to_bf16_bits(np.array([0.5, 2.0, 0.25], np.float32))[None]          # [1][N]
+    got = oracle.expand_matrix(q, s, oracle.FP8, oracle.BF16, 2, 3, 2, 0)
+    want = np.array([[1.0 * 0.5, -1.0 * 2.0, 1.5 * 0.25], [2.0 * 0.5, 0.0, 448.0 * 0.25]])
+    assert np.array_equal(got, want)
+
+
+def test_fp8_quantiser_error_and_layer_equals_dense_fp32_of_decoded_weights():
+    """Quantiser: |w - q s| <= s * 2^-4 * 2^e (half an e4m3 ulp) per element; the layer on fp8
+    weights equals the layer on the same weights decoded exactly and passed as fp32 dense weights
+    (bf16 x given as its exact fp32 values)."""
+    cfg = W.MoEConfig("fp8pin", T=24, H=64, E=8, k=2, I=64, e_first=0, e_local=8, wfmt="fp8")
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((64, 64)) / 8).astype(np.float32)
+    q, sb = W.quantize_fp8_e4m3_channel(w)
+    deq = oracle.expand_matrix(q[None], sb[None], oracle.FP8, oracle.BF16, 64, 64, 64, 0)
+    s = W.bf16_bits_to_f32(sb).astype(np.float64)
+    r = w.astype(np.float64) / s[None, :]
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -6))) - 3)
+    assert np.all(np.abs(w - deq) <= s[None, :] * ulp / 2 * (1 + 1e-12))
+    inp = W.make_inputs(cfg)
+    ids, wts = oracle.route(inp["logits"], cfg.k)
+    dense = dict(inp)
+    for name, (K, N) in (("w_gate", (64, 64)), ("w_up", (64, 64)), ("w_down", (64, 64))):
+        dense[name] = np.stack([oracle.expand_matrix(inp[name], inp[name + "_scale"], oracle.FP8, oracle.BF16, K, N,
+                                                     K, e) for e in range(8)]).astype(np.float32)
+    assert all(np.array_equal(dense[n].astype(np.float64), np.stack(
+        [oracle.expand_matrix(inp[n], inp[n + "_scale"], oracle.FP8, oracle.BF16, 64, 64, 64, e) for e in range(8)]))
+        for n in ("w_gate", "w_up", "w_down"))                  # fp32 holds every decoded product exactly
+    dense["x"] = W.bf16_bits_to_f32(inp["x"])
+    a = oracle.layer(inp, cfg, ids, wts)
+    b = oracle.layer(dense, cfg.with_(act="f32", wfmt="dense"), ids, wts)
+    assert np.array_equal(a, b)
