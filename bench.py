@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed token-expert pairs/s + % of HBM/MFMA roofline, one device's MoE layer"
 HEADLINE = "skewed_shared"
-SUBS = ["tiny", "decode", "prefill", "w4a16"]
+SUBS = ["tiny", "decode", "prefill", "w4a16", "w4a16_decode", "w4a16_channel", "fp8_decode", "fp8_prefill"]
 EVENT_EVERY = 5                # timed steps per event-bracketed launch of the dominant kernel
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_16BIT_PEAK_TFS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
@@ -43,6 +43,14 @@ DESCR = {
                      "top-10, I=1024, shared I=1024, bf16",
     "w4a16": "W4A16 prefill EP share: T=8192, H=4096, 64 of 512 local, top-10, I=1024, int4 weights "
              "(group 128, bf16 scales), bf16 activations",
+    "w4a16_decode": "decode-shaped EP share with int4 expert weights (group 128, bf16 scales): T=512, "
+                    "H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
+    "w4a16_channel": "prefill-shaped EP share with channel-wise int4 expert weights (one bf16 scale per "
+                     "output column): T=8192, H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
+    "fp8_decode": "decode-shaped EP share with FP8 (e4m3) expert weights, one bf16 scale per output "
+                  "channel: T=512, H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
+    "fp8_prefill": "prefill-shaped EP share with FP8 (e4m3) expert weights, one bf16 scale per output "
+                   "channel: T=8192, H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
 }
 
 
@@ -75,7 +83,9 @@ def measured_traffic(workload: str, kernel: str):
 def weight_bytes(cfg, K: int, N: int) -> int:
     """Bytes of one K x N expert matrix as stored in HBM (int4 words + bf16 scales, or dense)."""
     if cfg.wfmt == "int4":
-        return K * N // 2 + (K // cfg.group_size) * N * 2
+        return K * N // 2 + (K // (cfg.group_size or K)) * N * 2
+    if cfg.wfmt == "fp8":
+        return K * N + N * 2
     return K * N * (2 if cfg.act == "bf16" else 4)
 
 

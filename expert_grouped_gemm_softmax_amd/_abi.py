@@ -10,7 +10,7 @@ from .build import LIB_PATH, INCLUDE
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_SCRATCH_TOO_SMALL = 0, 1, 2, 3, 4
 MOE_PERMUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
 MOE_DT_F32, MOE_DT_BF16, MOE_DT_F16 = 0, 1, 2
-MOE_W_DENSE, MOE_W_INT4_SYM_GROUP, MOE_W_DENSE_NK, MOE_W_DENSE_NK_F16 = 0, 1, 2, 3
+MOE_W_DENSE, MOE_W_INT4_SYM_GROUP, MOE_W_DENSE_NK, MOE_W_DENSE_NK_F16, MOE_W_FP8_E4M3 = 0, 1, 2, 3, 4
 MOE_OP_GATE_UP_SWIGLU, MOE_OP_DOWN = 0, 1
 
 

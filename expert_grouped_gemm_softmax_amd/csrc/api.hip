@@ -144,10 +144,11 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (a->op != MOE_OP_GATE_UP_SWIGLU && a->op != MOE_OP_DOWN) return MOE_ERR_INVALID_ARG;
   if (!is_dtype(a->act_dtype) || !is_dtype(a->out_dtype)) return MOE_ERR_UNSUPPORTED;
   if (a->wfmt != MOE_W_DENSE && a->wfmt != MOE_W_INT4_SYM_GROUP && a->wfmt != MOE_W_DENSE_NK &&
-      a->wfmt != MOE_W_DENSE_NK_F16)
+      a->wfmt != MOE_W_DENSE_NK_F16 && a->wfmt != MOE_W_FP8_E4M3)
     return MOE_ERR_UNSUPPORTED;
   const bool gu = a->op == MOE_OP_GATE_UP_SWIGLU;
   const bool q4 = a->wfmt == MOE_W_INT4_SYM_GROUP;
+  const bool w8 = a->wfmt == MOE_W_FP8_E4M3;
   if (!a->a || !a->group_offsets || !a->w0 || !a->out) return MOE_ERR_INVALID_ARG;
   if (gu ? !a->w1 : a->w1 != nullptr) return MOE_ERR_INVALID_ARG;
   if (a->K < 64 || a->K % 64 != 0 || a->N < 64) return MOE_ERR_INVALID_ARG;
@@ -155,8 +156,8 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   if (a->n_groups < 1 || a->n_groups > 1024) return MOE_ERR_INVALID_ARG;
   if (a->rows_cap < 1 || a->a_rows < 1 || a->row_div < 1 || a->m_hint < 0) return MOE_ERR_INVALID_ARG;
   if (!a->row_index && a->a_rows < a->rows_cap) return MOE_ERR_INVALID_ARG;
-  if (q4) {
-    if (!a->s0 || (gu && !a->s1)) return MOE_ERR_INVALID_ARG;
+  if (q4 || w8) {
+    if (!a->s0 || (gu ? !a->s1 : a->s1 != nullptr)) return MOE_ERR_INVALID_ARG;
   } else if (a->group_size != 0 || a->s0 || a->s1) {
     return MOE_ERR_INVALID_ARG;
   }
@@ -168,19 +169,20 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   } else if (gu) {
     if (a->out_dtype == MOE_DT_F32) return MOE_ERR_INVALID_ARG;
     if (a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-    if (q4 ? a->out_dtype != MOE_DT_F16 : a->wfmt != MOE_W_DENSE_NK) return MOE_ERR_UNSUPPORTED;
+    if (q4 ? a->out_dtype != MOE_DT_F16 : (a->wfmt != MOE_W_DENSE_NK && !w8)) return MOE_ERR_UNSUPPORTED;
   } else {
     if (a->out_dtype != MOE_DT_F32 && a->out_dtype != a->act_dtype) return MOE_ERR_INVALID_ARG;
-    if (a->act_dtype == MOE_DT_BF16 ? a->wfmt != MOE_W_DENSE_NK
-                                    : (a->wfmt != MOE_W_DENSE_NK_F16 && !q4))
+    if (!w8 && (a->act_dtype == MOE_DT_BF16 ? a->wfmt != MOE_W_DENSE_NK
+                                            : (a->wfmt != MOE_W_DENSE_NK_F16 && !q4)))
       return MOE_ERR_UNSUPPORTED;
   }
+  if (w8 && a->group_size != a->K) return MOE_ERR_UNSUPPORTED;   // one scale per output channel
   // 32-bit byte offsets inside a (below 2^31: offsets from 2^31 up mark rows that load nothing)
   // and inside one expert's weight matrix
   const long long esz = a->act_dtype == MOE_DT_F32 ? 4 : 2;
-  if ((long long)a->a_rows * a->K * esz >= (1LL << 31) || (long long)a->K * a->N * esz >= (1LL << 32))
+  if ((long long)a->a_rows * a->K * esz >= (1LL << 31) || (long long)a->K * a->N * (w8 ? 1 : esz) >= (1LL << 32))
     return MOE_ERR_UNSUPPORTED;
-  if (q4 && (a->group_size < 64 || a->group_size % 64 != 0 || a->K % a->group_size != 0))
+  if (q4 && (a->group_size < 8 || a->group_size % 8 != 0 || a->K % a->group_size != 0))
     return MOE_ERR_UNSUPPORTED;
   return enqueue([&] { return moe::launch_grouped_gemm(*a, as_stream(stream)); });
 }

@@ -162,11 +162,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // converted to fp16 on its way to LDS.  int4 weights always run on fp16 operands.
 // SUM_ (with GU_): the epilogue writes acc0 + acc1 (+ bias) in fp32 instead of SwiGLU: the router
 // projection over an fp32 weight split into two bf16 planes.
+// W8_: fp8 (e4m3) weights [e][N][K], converted exactly to the operand type (bf16 or fp16) on their
+// way to LDS, with one scale per output column applied in the epilogue.
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1, int REGSETS_ = 2,
-          bool F16_ = Q4_, bool ACVT_ = false, bool SUM_ = false>
+          bool F16_ = Q4_, bool ACVT_ = false, bool SUM_ = false, bool W8_ = false>
 struct Cfg {
-  static constexpr bool F16 = F16_, ACVT = ACVT_, SUM = SUM_;
-  static constexpr float OUT_MUL = F16_ ? 1.0f / kF16WeightScale : 1.0f;
+  static constexpr bool F16 = F16_, ACVT = ACVT_, SUM = SUM_, W8 = W8_;
+  // fp16 operands carry weights scaled by 2^8 (int4, prepared dense fp16), fp8 ones do not
+  static constexpr float OUT_MUL = (F16_ && !W8_) ? 1.0f / kF16WeightScale : 1.0f;
   // Chunks held in registers between their loads and their LDS stores (two LDS buffers only).
   static constexpr int REGSETS = REGSETS_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
@@ -198,8 +201,10 @@ struct Cfg {
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
   static_assert(Q4 || BN % SLICE_ROWS == 0, "a dense piece slice stays inside one weight matrix");
   static_assert(!Q4 || F16, "int4 weights are dequantised to fp16");
+  static_assert(!W8_ || !ACVT, "fp8 weights convert to the activations' 16-bit type");
   static_assert(!ACVT || F16, "activations are converted to the fp16 operand type");
-  static_assert(!SUM || (GU && !Q4 && !F16), "router sums: two dense bf16 weight planes");
+  static_assert(!SUM || (GU && !Q4 && !F16 && !W8_), "router sums: two dense bf16 weight planes");
+  static_assert(!(Q4 && W8_), "one weight format");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
 
@@ -220,7 +225,7 @@ struct AChunk {
 };
 template <class C>
 struct WChunk {
-  u32x4 b[C::B_UNITS][C::Q4 ? 1 : C::R];
+  u32x4 b[C::B_UNITS][C::Q4 ? 1 : (C::W8 ? 2 : C::R)];   // int4: 4 words; fp8: 32 bytes; dense: R pieces
   u32x2 s[C::B_UNITS];
 };
 template <class C>
@@ -243,8 +248,11 @@ struct TileCtx {
   int b_lds;                                        // dense: LDS destination of the lane's first piece
   uint32_t b_off[C::B_UNITS];                       // int4: word offset of the unit
   uint32_t s_off[C::B_UNITS];                       // int4: scale offset of the unit
-  int b_dst[C::B_UNITS][C::Q4 ? 4 : 1];             // int4: LDS destination of each dequantised column
+  int b_dst[C::B_UNITS][(C::Q4 || C::W8) ? 4 : 1];  // int4: LDS destination of each dequantised column;
+                                                    // fp8: of each 16-byte chunk of the unit
   bool b_swap[C::B_UNITS];                          // int4: columns written in swapped pairs
+  int b_k[C::B_UNITS];                              // int4: first k of the unit's word row in a chunk
+  const u16* es[C::NW];                             // fp8: scales of the tile's first column, per matrix
   int nK, row_bytes, s_row_bytes, group_size;
 };
 
@@ -263,7 +271,12 @@ __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& c
   kc = min(kc, t.nK - 1);
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
-    if constexpr (!C::Q4) {
+    if constexpr (C::W8) {
+      // 32 consecutive k of one column: K bytes per column, the chunk at byte kc * 64
+      const uint32_t o = t.b_off[i] + (uint32_t)kc * C::KC;
+      ch.b[i][0] = __builtin_amdgcn_raw_buffer_load_b128(t.wr[i], o, 0, 2);
+      ch.b[i][1] = __builtin_amdgcn_raw_buffer_load_b128(t.wr[i], o + 16, 0, 2);
+    } else if constexpr (!C::Q4) {
       // piece x = i*R + r covers weight rows SLICE_ROWS*x .. SLICE_ROWS*(x+1)-1 of the NW*BN tile rows
 #pragma unroll
       for (int r = 0; r < C::R; ++r) {
@@ -275,7 +288,8 @@ __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& c
     } else {
       ch.b[i][0] = __builtin_amdgcn_raw_buffer_load_b128(
           t.wr[i], t.b_off[i] + (uint32_t)(kc * (C::KC / 8)) * t.row_bytes, 0, 2);
-      const int grp = (kc * C::KC) / t.group_size;
+      // the scale group of this unit's word row (groups of 8 k or more: one per word at least)
+      const int grp = (kc * C::KC + t.b_k[i]) / t.group_size;
       ch.s[i] = __builtin_amdgcn_raw_buffer_load_b64(t.sr[i], t.s_off[i] + (uint32_t)grp * t.s_row_bytes, 0, 0);
     }
   }
@@ -328,12 +342,31 @@ __device__ __forceinline__ f16x2 scale_f16x2(uint32_t sbits) {
   return f16x2{h, h};
 }
 
+// Four fp8 values (one dword, k ascending) -> two dwords of 16-bit operands, exactly (e4m3's 4
+// significant bits and exponent range fit bf16 and fp16).
+template <bool F16>
+__device__ __forceinline__ u32x2 fp8x4_to_16(uint32_t d) {
+  if constexpr (F16)
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true))};
+  else
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true))};
+}
+
 template <class C>
 __device__ __forceinline__ void store_w(const TileCtx<C>& t, const WChunk<C>& ch, u16* buf) {
   u16* sB = buf + C::A_ELEMS;
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
-    if constexpr (!C::Q4) {
+    if constexpr (C::W8) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {                  // eight k per 16-byte LDS chunk
+        const u32x2 lo = fp8x4_to_16<C::F16>(ch.b[i][c >> 1][2 * (c & 1)]);
+        const u32x2 hi = fp8x4_to_16<C::F16>(ch.b[i][c >> 1][2 * (c & 1) + 1]);
+        *reinterpret_cast<u32x4*>(sB + t.b_dst[i][c]) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else if constexpr (!C::Q4) {
 #pragma unroll
       for (int r = 0; r < C::R; ++r)
         *reinterpret_cast<u32x4*>(sB + t.b_lds + C::SLICE_ROWS * (i * C::R + r) * 64) = ch.b[i][r];
@@ -489,14 +522,19 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
         const int row = wrow0 + i * 16 * C::WM + (lane >> 4) * 4 + r;
         const int col = wcol0 + j * 16 + (lane & 15);
         if (row < rows) {
+          float m0 = C::OUT_MUL, m1 = C::OUT_MUL;
+          if constexpr (C::W8) {                     // fp8: the output column's scales
+            m0 = bf16_to_f32(t.es[0][col]);
+            if constexpr (C::NW == 2) m1 = bf16_to_f32(t.es[C::NW - 1][col]);
+          }
           float v;
           if constexpr (C::SUM) {
             v = acc[0][i][j][r] + acc[1][i][j][r];
             if (bias) v = v + bias[n0 + col];
           } else if constexpr (C::GU) {
-            v = silu_mul(acc[0][i][j][r] * C::OUT_MUL, acc[1][i][j][r] * C::OUT_MUL);
+            v = silu_mul(acc[0][i][j][r] * m0, acc[1][i][j][r] * m1);
           } else {
-            v = acc[0][i][j][r] * C::OUT_MUL;
+            v = acc[0][i][j][r] * m0;
           }
           store_out(O + (size_t)(row0 + row) * N + n0 + col, v);
         }
@@ -537,7 +575,8 @@ void k_gemm_bf16(GemmParams p) {
   // the host checks a_rows * K * 2 < 2^32
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, (uint32_t)((size_t)p.a_rows * p.K * 2));
   OutT* O = static_cast<OutT*>(p.out);
-  const uint32_t w_bytes = C::Q4 ? (uint32_t)((size_t)p.K / 8 * p.N * 4) : (uint32_t)((size_t)p.K * p.N * 2);
+  const uint32_t w_bytes = C::Q4 ? (uint32_t)((size_t)p.K / 8 * p.N * 4)
+                                 : (uint32_t)((size_t)p.K * p.N * (C::W8 ? 1 : 2));
   const uint32_t s_bytes = C::Q4 ? (uint32_t)((size_t)(p.K / p.group_size) * p.N * 2) : 0u;
 
   for (int tile = it.next; tile < it.end; tile += it.step) {
@@ -562,7 +601,25 @@ void k_gemm_bf16(GemmParams p) {
     }
     // piece i of a thread lands SLICE_ROWS * i rows below piece 0 (the swizzle repeats every 16 rows)
     t.a_lds = lds_off_rows((tid % C::A_CHUNKS) / (KC / 8), tid % (KC / 8));
-    if constexpr (!C::Q4) {
+    if constexpr (C::W8) {
+      // fp8 [e][n][k]: unit u of a matrix covers k = 32 (u % 2) .. + 31 of column u / 2, so two
+      // lanes read one column's 64 bytes of a chunk; each 16-lane LDS pass writes 8 columns (4
+      // even, 4 odd rows) at two chunk positions each, one per bank group.
+      constexpr int per_m = KC * BN / 32;
+      static_assert(per_m % 64 == 0, "a wave's units read one matrix");
+#pragma unroll
+      for (int i = 0; i < C::B_UNITS; ++i) {
+        const int m = __builtin_amdgcn_readfirstlane((tid + NT * i) / per_m);
+        t.wr[i] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)e * w_bytes, w_bytes);
+        const int u = (tid + NT * i) % per_m, n = u / 2, kq = u % 2;
+        t.b_off[i] = (uint32_t)((n0 + n) * p.K + kq * 32);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t.b_dst[i][c] = lds_off_rows(m * BN + n, kq * 4 + c);
+      }
+#pragma unroll
+      for (int m = 0; m < C::NW; ++m)
+        t.es[m] = static_cast<const u16*>(m == 0 ? p.s0 : p.s1) + (size_t)e * p.N + n0;
+    } else if constexpr (!C::Q4) {
       // Weight rows are K-contiguous ([e][n][k]) and go to LDS like activation rows: 8 lanes per
       // 128-byte row chunk, wave w's lanes on rows 8w .. 8w+7 of every slice of SLICE_ROWS rows.
 #pragma unroll
@@ -599,6 +656,7 @@ void k_gemm_bf16(GemmParams p) {
         t.b_off[i] = (uint32_t)(kw * p.N + n0 + nq * 4) * 4u;
         t.s_off[i] = (uint32_t)(n0 + nq * 4) * 2u;
         t.b_swap[i] = sw != 0;
+        t.b_k[i] = kw * 8;
 #pragma unroll
         for (int c = 0; c < 4; ++c) t.b_dst[i][c] = lds_off_rows(m * BN + nq * 4 + (c ^ sw), kw);
       }
@@ -1292,7 +1350,7 @@ hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  if constexpr (C::STAGES == 1 && !C::Q4 && !C::SUM) {
+  if constexpr (C::STAGES == 1 && !C::Q4 && !C::SUM && !C::W8) {
     if (p.row_index == nullptr && (p.K / C::KC) % 2 == 0) {
       k_gemm_stream<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
       return hipGetLastError();
@@ -1339,18 +1397,18 @@ constexpr bool cfg_ok() {
 //            operands, activations converted); int4 needs fp16 h;
 //   down:    bf16 h with bf16 weights (bf16 operands) or fp16 h with fp16 or int4 weights (fp16
 //            operands); out in fp32 or h's dtype.
-template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS, bool Q4, bool F16, typename OutT>
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS, bool Q4, bool F16, typename OutT, bool W8 = false>
 hipError_t run_cfg_gu(const GemmParams& p, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, true>(), "gate/up tile");
-  using C = Cfg<BM, BN, WM, WN, ST, true, Q4, WGS, RS, F16, F16>;
+  using C = Cfg<BM, BN, WM, WN, ST, true, Q4, WGS, RS, F16, F16, false, W8>;
   static_assert(C::STAGES * C::STAGE * 2 + 2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
   return run_bf16<C, OutT>(p, WGS, s);
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS, bool Q4, bool F16, typename OutT>
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS, bool Q4, bool F16, typename OutT, bool W8 = false>
 hipError_t run_cfg_dn(const GemmParams& p, hipStream_t s) {
   static_assert(cfg_ok<BM, BN, WM, WN, false>(), "down tile");
-  using C = Cfg<BM, BN, WM, WN, ST, false, Q4, WGS, RS, F16, false>;
+  using C = Cfg<BM, BN, WM, WN, ST, false, Q4, WGS, RS, F16, false, false, W8>;
   static_assert(C::STAGES * C::STAGE * 2 + 2 * 4 * 1025 + 16 <= kLdsPerCu, "LDS");
   return run_bf16<C, OutT>(p, WGS, s);
 }
@@ -1378,6 +1436,22 @@ hipError_t run_dn(const GemmParams& p, bool q4, bool f16, bool f32out, hipStream
                   : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, true, _Float16>(p, s);
   return f32out ? run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, false, float>(p, s)
                 : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, false, u16>(p, s);
+}
+
+// fp8 weights, one tile shape: gate/up on bf16 operands (h bf16 or fp16); down on the operand type
+// of h (bf16 or fp16), out fp32 or h's dtype
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS>
+hipError_t run_gu_w8(const GemmParams& p, bool h16, hipStream_t s) {
+  return h16 ? run_cfg_gu<BM, BN, WM, WN, ST, WGS, RS, false, false, _Float16, true>(p, s)
+             : run_cfg_gu<BM, BN, WM, WN, ST, WGS, RS, false, false, u16, true>(p, s);
+}
+template <int BM, int BN, int WM, int WN, int ST, int WGS, int RS>
+hipError_t run_dn_w8(const GemmParams& p, bool f16, bool f32out, hipStream_t s) {
+  if (f16)
+    return f32out ? run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, true, float, true>(p, s)
+                  : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, true, _Float16, true>(p, s);
+  return f32out ? run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, false, float, true>(p, s)
+                : run_cfg_dn<BM, BN, WM, WN, ST, WGS, RS, false, false, u16, true>(p, s);
 }
 
 // dense prefill-shaped down projection with direct global -> LDS loads
@@ -1408,6 +1482,16 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool h16 = a.out_dtype == MOE_DT_F16;
   // The ABI guarantees N % 64 == 0 (gate/up) and N % 128 == 0 (down): variants 0 and 2 always fit.
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
+  if (a.wfmt == MOE_W_FP8_E4M3) {
+    if (gu) {
+      if (small_m) return run_gu_w8<32, 64, 1, 4, 1, 4, 2>(p, h16, s);
+      if (p.N % 128 == 0) return run_gu_w8<192, 128, 4, 2, 2, 1, 1>(p, h16, s);
+      return run_gu_w8<256, 64, 4, 1, 2, 1, 2>(p, h16, s);
+    }
+    if (small_m) return run_dn_w8<32, 128, 1, 4, 1, 4, 2>(p, f16, f32out, s);
+    // 4-wave 256 x 128 tiles: the 8-wave 256 x 256 tile needs more than two waves' registers
+    return run_dn_w8<256, 128, 4, 1, 2, 1, 2>(p, f16, f32out, s);
+  }
   if (gu) {
     if (small_m) return run_gu<32, 64, 1, 4, 1, 4, 2>(p, q4, h16, s);
     if (p.N % 128 == 0) {

@@ -20,7 +20,9 @@ class ExpertWeights:
     from the stated [e_local][K][N]; see upload): w_gate, w_up [e_local][I][H] in the activation
     dtype, w_down [e_local][H][I] in the dtype of the SwiGLU output h (fp16 holding 2^8 * W by
     default, or bf16); shared expert gate, up [Is][H], down [H][Is] likewise.
-    int4: int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N]; h is fp16."""
+    int4: int32 words [e_local][K/8][N] plus bf16 scales [e_local][K/group_size][N] (group_size 0:
+    channel-wise, one scale per column over all K); h is fp16.  fp8: e4m3 bytes [e_local][N][K]
+    plus bf16 scales [e_local][N]; h fp16 (or bf16)."""
     w_gate: torch.Tensor
     w_up: torch.Tensor
     w_down: torch.Tensor
@@ -32,19 +34,27 @@ class ExpertWeights:
     shared_up: torch.Tensor | None = None
     shared_down: torch.Tensor | None = None
 
+    h_fp8: torch.dtype = torch.float16   # h's dtype over fp8 down weights (fp16 or bf16)
+
     @property
     def int4(self) -> bool:
         return self.w_gate.dtype == torch.int32
 
     @property
+    def fp8(self) -> bool:
+        return self.w_gate.dtype == torch.uint8
+
+    @property
     def h_dtype(self) -> torch.dtype:
         """dtype of the SwiGLU output h between the two GEMMs: fp16 over fp16 or int4 down weights
-        (the fp16 MFMA path), else the down weights' dtype."""
-        return torch.float16 if self.int4 else self.w_down.dtype
+        (the fp16 MFMA path), either 16-bit type over fp8 ones, else the down weights' dtype."""
+        if self.int4:
+            return torch.float16
+        return self.h_fp8 if self.fp8 else self.w_down.dtype
 
 
 def _t(a: np.ndarray, device) -> torch.Tensor:
-    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns, uint8 arrays fp8 bytes."""
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
@@ -68,11 +78,12 @@ def upload(inputs: dict, cfg, device="cuda", h_dtype=torch.float16) -> tuple[tor
             return ops.prepare_dense_weights_f16(w)
         return ops.prepare_dense_weights(w)
 
-    if cfg.wfmt == "int4":
+    if cfg.wfmt in ("int4", "fp8"):
         kw = dict(w_gate=_t(inputs["w_gate"], device), w_up=_t(inputs["w_up"], device),
                   w_down=_t(inputs["w_down"], device),
                   s_gate=_t(inputs["w_gate_scale"], device), s_up=_t(inputs["w_up_scale"], device),
-                  s_down=_t(inputs["w_down_scale"], device), group_size=cfg.group_size)
+                  s_down=_t(inputs["w_down_scale"], device),
+                  group_size=cfg.group_size if cfg.wfmt == "int4" else 0, h_fp8=h_dtype)
     else:
         kw = dict(w_gate=dense("w_gate"), w_up=dense("w_up"), w_down=dense_down("w_down"))
     if cfg.shared_I:
@@ -128,6 +139,9 @@ class MoELayer:
                              "prepare_dense_weights_f16")
         if W.int4:
             want = {"w_gate": (el, H // 8, I), "w_up": (el, H // 8, I), "w_down": (el, I // 8, H)}
+        elif W.fp8:
+            want = {"w_gate": (el, I, H), "w_up": (el, I, H), "w_down": (el, H, I),
+                    "s_gate": (el, I), "s_up": (el, I), "s_down": (el, H)}
         else:
             want = {"w_gate": (el, I, H), "w_up": (el, I, H), "w_down": (el, H, I)}
         if self.shared_I:
@@ -179,12 +193,14 @@ class MoELayer:
         W = self.weights
         ops.grouped_gemm(_abi.MOE_OP_GATE_UP_SWIGLU, x, b.group_offsets, W.w_gate, W.w_up, b.h,
                          K=self.H, N=self.I, row_index=b.sorted_pairs, row_div=self.k, s0=W.s_gate,
-                         s1=W.s_up, group_size=W.group_size, m_hint=self.m_hint(x.shape[0]), stream=stream)
+                         s1=W.s_up, group_size=W.group_size or self.H, m_hint=self.m_hint(x.shape[0]),
+                         stream=stream)
 
     def step_down(self, x, b, stream=None):
         W = self.weights
         ops.grouped_gemm(_abi.MOE_OP_DOWN, b.h, b.group_offsets, W.w_down, None, b.o, K=self.I, N=self.H,
-                         s0=W.s_down, group_size=W.group_size, m_hint=self.m_hint(x.shape[0]), stream=stream)
+                         s0=W.s_down, group_size=W.group_size or self.I, m_hint=self.m_hint(x.shape[0]),
+                         stream=stream)
 
     def step_shared(self, x, b, stream=None):
         W, T = self.weights, x.shape[0]

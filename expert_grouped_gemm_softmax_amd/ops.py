@@ -191,18 +191,21 @@ def grouped_gemm(op: int, a: torch.Tensor, group_offsets: torch.Tensor, w0: torc
     [n_groups][N][K] (weights_nk, from prepare_dense_weights) or [n_groups][K][N] (fp32 only) in the
     activation dtype, or fp16 [n_groups][N][K] from prepare_dense_weights_f16 (down projection over
     fp16 h); int4 weights are int32 words [n_groups][K/8][N] with bf16 scales s0/s1
-    [n_groups][K/group_size][N]."""
+    [n_groups][K/group_size][N]; fp8 (e4m3) weights are uint8 [n_groups][N][K] with bf16 scales
+    s0/s1 [n_groups][N]."""
     _dev(a, group_offsets, w0, w1, out, row_index, s0, s1)
     args = _abi.MoeGemmArgs()
     args.op = op
     args.act_dtype = _DT[a.dtype]
     if w0.dtype == torch.int32:
         args.wfmt = _abi.MOE_W_INT4_SYM_GROUP
+    elif w0.dtype == torch.uint8:
+        args.wfmt = _abi.MOE_W_FP8_E4M3
     elif w0.dtype == torch.float16:
         args.wfmt = _abi.MOE_W_DENSE_NK_F16
     else:
         args.wfmt = _abi.MOE_W_DENSE_NK if weights_nk else _abi.MOE_W_DENSE
-    args.group_size = group_size if args.wfmt == _abi.MOE_W_INT4_SYM_GROUP else 0
+    args.group_size = {_abi.MOE_W_INT4_SYM_GROUP: group_size, _abi.MOE_W_FP8_E4M3: K}.get(args.wfmt, 0)
     args.K, args.N = K, N
     args.n_groups = group_offsets.numel() - 1
     args.rows_cap = out.shape[0]

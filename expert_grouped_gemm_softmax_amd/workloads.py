@@ -42,7 +42,7 @@ class MoEConfig:
     e_local: int
     act: str = "bf16"          # "f32" or "bf16": activations and dense weights
     wfmt: str = "dense"        # "dense", "int4" or "fp8" (OCP e4m3, one scale per output channel)
-    group_size: int = 128      # int4 quantisation group along K
+    group_size: int = 128      # int4 quantisation group along K (0: channel-wise, one group of K rows)
     shared_I: int = 0          # intermediate size of the always-on shared expert (0: none)
     zipf_bias: float = 0.0     # additive logit bias zipf_bias * ln(1 / (e + 1)) per expert
     seed: int = 0
@@ -64,6 +64,12 @@ CONFIGS = {
     # Prefill shapes with symmetric int4 expert weights, groups of 128 along K, bf16 scales.
     "w4a16": MoEConfig("w4a16", T=8192, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
                        wfmt="int4", group_size=128),
+    # The int4 format at the decode shape, and channel-wise int4 scales (one group of K rows) at
+    # the prefill shape.
+    "w4a16_decode": MoEConfig("w4a16_decode", T=512, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
+                              wfmt="int4", group_size=128),
+    "w4a16_channel": MoEConfig("w4a16_channel", T=8192, H=4096, E=512, k=10, I=1024, e_first=0,
+                               e_local=64, wfmt="int4", group_size=0),
     # Decode and prefill shapes with FP8 (e4m3) expert weights, one bf16 scale per output channel.
     "fp8_decode": MoEConfig("fp8_decode", T=512, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
                             wfmt="fp8"),
@@ -201,7 +207,7 @@ def make_inputs(cfg: MoEConfig, *, tie_quantum: float | None = None,
         seed, shape, fan_in = args
         w = _normal(seed, shape, 1.0 / math.sqrt(fan_in))
         if cfg.wfmt == "int4":
-            q, s_bits = quantize_int4_sym(w, cfg.group_size)
+            q, s_bits = quantize_int4_sym(w, cfg.group_size or shape[0])
             return pack_int4(q), s_bits
         if cfg.wfmt == "fp8":
             return quantize_fp8_e4m3_channel(w)

@@ -69,12 +69,18 @@ typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_F16 = 2 } moe_d
  * activation-order variants are not supported there and are not representable here).
  * Layout for a [K][N] matrix of expert e: words int32 [E][K/8][N], the two's-complement nibble at
  * bits 4i..4i+3 of word [e][kb][n] is q[8*kb+i][n]; scales bf16 [E][K/group_size][N];
- * weight = q * scale.  Channel-wise scales are group_size == K. */
+ * weight = q * scale.  Channel-wise scales are group_size == K.
+ * MOE_W_FP8_E4M3: 8-bit floating-point weights (the FP8-served models of "vLLM TPU Inference
+ * v0.31.0", inter-chip transfer split), read as OCP E4M3 (bias 7, no infinities, S.1111.111 NaN)
+ * bytes stored [E][N][K] (each output column's K weights contiguous, the [out][in] orientation of
+ * a linear layer) with one bf16 scale per output column, [E][N]; weight = e4m3(q) * scale;
+ * group_size must be K. */
 typedef enum moe_wfmt {
   MOE_W_DENSE = 0,
   MOE_W_INT4_SYM_GROUP = 1,
   MOE_W_DENSE_NK = 2,
-  MOE_W_DENSE_NK_F16 = 3
+  MOE_W_DENSE_NK_F16 = 3,
+  MOE_W_FP8_E4M3 = 4
 } moe_wfmt;
 
 typedef enum moe_gemm_op {
@@ -214,11 +220,13 @@ moe_status moe_permute_noalloc(const int32_t* blob, int T, int k, int e_first, i
  * Supported combinations (anything else is MOE_ERR_UNSUPPORTED; MOE_W_DENSE with 16-bit
  * activations is prepared once with moe_prepare_dense_weights[_f16]):
  *   fp32:     a, weights (MOE_W_DENSE or MOE_W_DENSE_NK) and out fp32; vector-ALU fp32 arithmetic.
- *   GATE_UP:  a = x bf16; MOE_W_DENSE_NK bf16 weights (bf16 MFMA operands) with out (h) bf16 or
- *             fp16, or MOE_W_INT4_SYM_GROUP with out fp16.
+ *   GATE_UP:  a = x bf16; MOE_W_DENSE_NK bf16 or MOE_W_FP8_E4M3 weights (bf16 MFMA operands) with
+ *             out (h) bf16 or fp16, or MOE_W_INT4_SYM_GROUP with out fp16.
  *   DOWN:     a = h bf16 with MOE_W_DENSE_NK bf16 weights (bf16 operands), or a = h fp16 with
- *             MOE_W_DENSE_NK_F16 or MOE_W_INT4_SYM_GROUP weights (fp16 operands); out fp32 or a's
- *             dtype.
+ *             MOE_W_DENSE_NK_F16 or MOE_W_INT4_SYM_GROUP weights (fp16 operands), or a = h bf16 or
+ *             fp16 with MOE_W_FP8_E4M3 weights (operands in h's dtype); out fp32 or a's dtype.
+ * fp8 weights convert exactly to bf16 and to fp16 (4 significant bits; exponents 2^-9..2^8) on
+ * their way to LDS; their per-column scales multiply the fp32 accumulators in the epilogue.
  * Accumulation is fp32 throughout.  int4 weights run on fp16 operands: each weight q * s is
  * dequantised exactly to fp16 in LDS (q * s has at most 11 significant bits, which bf16 would
  * round), as 2^8 * q * s, exact for scales 2^-22 <= s < 32; their bf16 activations x are converted
@@ -233,7 +241,8 @@ typedef struct moe_gemm_args {
   int32_t op;          /* moe_gemm_op */
   int32_t act_dtype;   /* moe_dtype of a (and of dense MOE_W_DENSE / MOE_W_DENSE_NK weights) */
   int32_t wfmt;        /* moe_wfmt of w0 / w1 (int4 requires MOE_DT_BF16) */
-  int32_t group_size;  /* int4: K rows per scale; a multiple of 64 that divides K.  Dense: 0 */
+  int32_t group_size;  /* int4: K rows per scale; a multiple of 8 that divides K (K: channel-wise).
+                          fp8: K.  Dense: 0 */
   int32_t K;           /* contraction length: H for GATE_UP, I for DOWN; multiple of 64 */
   int32_t N;           /* output columns: I for GATE_UP (multiple of 64), H for DOWN (multiple
                           of 128) */
@@ -248,8 +257,9 @@ typedef struct moe_gemm_args {
   const int32_t* group_offsets;  /* [n_groups+1] non-decreasing, [0] = 0 (e.g. from moe_permute) */
   const void* w0;      /* GATE_UP: Wg; DOWN: Wd, in format wfmt (see moe_wfmt) */
   const void* w1;      /* GATE_UP: Wu (same layout as w0); DOWN: NULL */
-  const void* s0;      /* int4: bf16 scales of w0 [n_groups][K/group_size][N]; dense: NULL */
-  const void* s1;      /* int4: bf16 scales of w1; otherwise NULL */
+  const void* s0;      /* int4: bf16 scales of w0 [n_groups][K/group_size][N]; fp8: bf16 [n_groups][N];
+                          dense: NULL */
+  const void* s1;      /* int4, fp8 GATE_UP: scales of w1 (as s0); otherwise NULL */
   void* out;           /* [rows_cap][N] out_dtype */
 } moe_gemm_args;
 

@@ -293,7 +293,7 @@ typedef struct {
   int T, H, I, k, e_first, e_local;
   int act;          /* ORC_F32 or ORC_BF16: x, dense weights, shared weights */
   int wfmt;         /* ORC_DENSE, ORC_INT4 or ORC_FP8 for the routed experts */
-  int group_size;   /* int4 group along K */
+  int group_size;   /* int4 group along K; <= 0: channel-wise (all K rows of a matrix) */
   int shared_I;     /* 0: no shared expert */
   const void* x;    /* [T][H] */
   const int32_t* ids;   /* [T][k] global expert ids */
@@ -314,9 +314,11 @@ void orc_layer(const orc_layer_args* A, const int32_t* tokens, int n_tokens, dou
   double* uacc = (double*)malloc(sizeof(double) * (size_t)Imax);
   double* row = (double*)malloc(sizeof(double) * (size_t)wide);
   double* o = (double*)malloc(sizeof(double) * (size_t)H);
-  orc_mat g = {A->wg, A->sg, A->wfmt, A->act, H, I, A->group_size};
-  orc_mat u = {A->wu, A->su, A->wfmt, A->act, H, I, A->group_size};
-  orc_mat d = {A->wd, A->sd, A->wfmt, A->act, I, H, A->group_size};
+  /* group_size <= 0: channel-wise scales, one group of all K rows of a matrix */
+  const int gs_in = A->group_size > 0 ? A->group_size : H, gs_out = A->group_size > 0 ? A->group_size : I;
+  orc_mat g = {A->wg, A->sg, A->wfmt, A->act, H, I, gs_in};
+  orc_mat u = {A->wu, A->su, A->wfmt, A->act, H, I, gs_in};
+  orc_mat d = {A->wd, A->sd, A->wfmt, A->act, I, H, gs_out};
   orc_mat sg = {A->shg, NULL, ORC_DENSE, A->act, H, A->shared_I, 1};
   orc_mat su = {A->shu, NULL, ORC_DENSE, A->act, H, A->shared_I, 1};
   orc_mat sd = {A->shd, NULL, ORC_DENSE, A->act, A->shared_I, H, 1};

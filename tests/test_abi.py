@@ -138,8 +138,9 @@ def _gemm(**kw):
     (dict(n_groups=0), INV), (dict(n_groups=1025), INV), (dict(rows_cap=0), INV), (dict(a_rows=0), INV),
     (dict(row_div=0), INV), (dict(m_hint=-1), INV), (dict(row_index=None, a_rows=10), INV),
     (dict(wfmt=1, act_dtype=0, out_dtype=0, group_size=128, s0=FAKE, s1=FAKE), UNS),
-    (dict(wfmt=1, out_dtype=2, group_size=32, s0=FAKE, s1=FAKE), UNS),
-    (dict(wfmt=1, out_dtype=2, group_size=96, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, out_dtype=2, group_size=20, s0=FAKE, s1=FAKE), UNS),      # not whole words
+    (dict(wfmt=1, out_dtype=2, group_size=4, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=1, out_dtype=2, group_size=96, s0=FAKE, s1=FAKE), UNS),      # does not divide K
     (dict(wfmt=1, out_dtype=2, K=192, group_size=128, s0=FAKE, s1=FAKE), UNS),
     # int4 runs on fp16 operands: gate/up writes fp16 h, down reads fp16 h
     (dict(wfmt=1, out_dtype=1, group_size=128, s0=FAKE, s1=FAKE), UNS),
@@ -150,6 +151,12 @@ def _gemm(**kw):
     (dict(op=1, K=128, N=256, w1=None, wfmt=3, act_dtype=2, out_dtype=1), INV),
     (dict(act_dtype=2, out_dtype=2), UNS), (dict(wfmt=3, out_dtype=2), UNS),
     (dict(act_dtype=0, out_dtype=0, wfmt=3), UNS),
+    # fp8: scales required (two for gate/up, one for down), one per output channel (group = K)
+    (dict(wfmt=4, out_dtype=2, group_size=256), INV), (dict(wfmt=4, out_dtype=2, group_size=256, s0=FAKE), INV),
+    (dict(op=1, K=128, N=256, w1=None, wfmt=4, act_dtype=2, out_dtype=0, group_size=128, s0=FAKE, s1=FAKE), INV),
+    (dict(wfmt=4, out_dtype=2, group_size=128, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=4, act_dtype=0, out_dtype=0, group_size=256, s0=FAKE, s1=FAKE), UNS),
+    (dict(wfmt=4, act_dtype=2, out_dtype=2, group_size=256, s0=FAKE, s1=FAKE), UNS),
     (dict(wfmt=1, group_size=128, s0=None, s1=FAKE), INV),
     (dict(wfmt=1, group_size=128, s0=FAKE, s1=None), INV),
     (dict(group_size=128), INV), (dict(s0=FAKE), INV),

@@ -218,6 +218,11 @@ MID = {
                              wfmt="int4", group_size=128),
     "int4_channel": W.MoEConfig("mid", T=150, H=256, E=16, k=3, I=256, e_first=2, e_local=8,
                                     wfmt="int4", group_size=256),
+    # groups narrower than a 64-k chunk: several scale rows per chunk, one per word row
+    "int4_g32": W.MoEConfig("mid", T=220, H=512, E=24, k=4, I=256, e_first=0, e_local=12,
+                            wfmt="int4", group_size=32),
+    "int4_g8": W.MoEConfig("mid", T=90, H=256, E=8, k=2, I=128, e_first=0, e_local=8,
+                           wfmt="int4", group_size=8),
     # decode-shaped tiles with about 40 rows per expert: two 32-row tiles per expert, so the down
     # projection has four tiles per workgroup and its loads run across three tile boundaries
     "bf16_many_tiles_per_workgroup": W.MoEConfig("mid", T=320, H=4096, E=64, k=8, I=256, e_first=0,
@@ -227,13 +232,16 @@ MID = {
     # the most local experts the library accepts: tile tables of 1024 groups (the prefill down
     # projection falls back to the LDS tile table)
     "bf16_1024_local_experts": W.MoEConfig("mid", T=600, H=256, E=1024, k=8, I=128, e_first=0, e_local=1024),
+    # fp8 (e4m3) weights with per-column scales, converted exactly to the 16-bit operand type
+    "fp8": W.MoEConfig("mid", T=260, H=512, E=32, k=4, I=384, e_first=0, e_local=16, wfmt="fp8"),
+    "fp8_many_tiles": W.MoEConfig("mid", T=300, H=1024, E=64, k=8, I=256, e_first=8, e_local=40, wfmt="fp8"),
     "f32": W.MoEConfig("mid", T=130, H=256, E=12, k=3, I=192, e_first=1, e_local=9, act="f32"),
     "f32_shared": W.MoEConfig("mid", T=70, H=128, E=8, k=2, I=64, e_first=0, e_local=8, act="f32",
                               shared_I=128),
 }
 
 
-MID_BF16_H = [n for n, c in MID.items() if c.act == "bf16" and c.wfmt == "dense"]
+MID_BF16_H = [n for n, c in MID.items() if c.act == "bf16" and c.wfmt in ("dense", "fp8")]
 
 
 @pytest.mark.parametrize("variant", ["small_m", "large_m"])
@@ -386,7 +394,8 @@ def _both_families(cfg, inp):
     return ids, w, off, out
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "w4a16"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "w4a16", "w4a16_decode", "w4a16_channel",
+                                  "fp8_decode", "fp8_prefill"])
 def test_layer_full_workload_every_token(name):
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg, threads=16)

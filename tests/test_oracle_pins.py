@@ -208,7 +208,7 @@ def _dense_f64(inp, cfg, name):
             nib = ((words >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int64)
             q[:, i::8, :] = np.where(nib >= 8, nib - 16, nib)
         s = W.bf16_bits_to_f32(inp[name + "_scale"]).astype(np.float64)
-        return q * np.repeat(s, cfg.group_size, axis=1)
+        return q * np.repeat(s, cfg.group_size or Kb * 8, axis=1)       # 0: one group of all K rows
     if a.dtype == np.uint16:
         return W.bf16_bits_to_f32(a).astype(np.float64)
     return a.astype(np.float64)
@@ -251,6 +251,7 @@ def _tiny(**kw):
     _tiny(act="bf16", e_first=2, e_local=8, shared_I=24),
     _tiny(act="bf16", wfmt="int4", group_size=8, H=64, I=32, E=16, e_local=16, k=4),
     _tiny(act="bf16", wfmt="int4", group_size=64, H=64, I=64, e_first=3, e_local=6),
+    _tiny(act="bf16", wfmt="int4", group_size=0, H=96, I=48, e_first=1, e_local=7),     # channel-wise
     W.CONFIGS["tiny"],
 ])
 def test_layer_matches_dense_brute_force(cfg):
