@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed token-expert pairs/s + % of HBM/MFMA roofline, one device's MoE layer"
 HEADLINE = "skewed_shared"
-SUBS = ["tiny", "decode", "prefill", "w4a16", "w4a16_decode", "w4a16_channel", "fp8_decode", "fp8_prefill"]
+SUBS = ["tiny", "decode", "prefill", "w4a16", "w4a16_decode", "w4a16_channel", "w4a16_skewed", "fp8_decode",
+        "fp8_prefill"]
 EVENT_EVERY = 5                # timed steps per event-bracketed launch of the dominant kernel
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_16BIT_PEAK_TFS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
@@ -47,6 +48,8 @@ DESCR = {
                     "H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
     "w4a16_channel": "prefill-shaped EP share with channel-wise int4 expert weights (one bf16 scale per "
                      "output column): T=8192, H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
+    "w4a16_skewed": "Zipf-skewed routing + shared SwiGLU expert with int4 routed experts (group 128): "
+                    "T=8192, H=4096, 64 of 512 local, top-10, I=1024, shared I=1024 (bf16)",
     "fp8_decode": "decode-shaped EP share with FP8 (e4m3) expert weights, one bf16 scale per output "
                   "channel: T=512, H=4096, 64 of 512 local, top-10, I=1024, bf16 activations",
     "fp8_prefill": "prefill-shaped EP share with FP8 (e4m3) expert weights, one bf16 scale per output "
@@ -371,6 +374,22 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
     topk_us = float(np.mean([rev[i][1].elapsed_time(rev[i][2]) * 1e3 for i in range(nb)]))
     del wsplit, r_logits
 
+    # The same step with the dense weights left in their stated [e][K][N] layout (transposed
+    # operand reads, bf16 h) beside the prepared layout's
+    stated = None
+    if cfg.wfmt == "dense" and cfg.act == "bf16" and not cfg.shared_I:
+        xs, ls, kn = upload(inp, cfg, x.device, stated_layout=True)
+        lk = MoELayer.from_config(cfg, kn)
+        for _ in range(3):
+            lk.forward(xs, ls)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            lk.forward(xs, ls)
+        torch.cuda.synchronize()
+        stated = round((time.perf_counter() - t0) / K * 1e3, 4)
+        del lk, kn, xs, ls
+
     wk = work(cfg, n_loc, nonempty)
     roof = roofline(cfg, wk["gate_up"]["flops"], wk["gate_up"]["bytes"], gu_us * 1e-6, att)
     roof.update({"kernel": "routed grouped GEMM gate/up + SwiGLU", "time_us": round(gu_us, 1),
@@ -393,6 +412,7 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
         "roofline": roof,
         "kernels_us": {n: round(v, 1) for n, v in kus.items()},
         "kernel_rooflines": kernels,
+        "stated_layout_ms_per_step": stated,
         "router_from_hidden": {
             "projection_us": round(proj_us, 1), "route_packed_us": round(topk_us, 1),
             "projection_roofline": roofline(cfg, 2.0 * cfg.T * cfg.H * cfg.E,

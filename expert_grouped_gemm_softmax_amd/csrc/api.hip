@@ -169,10 +169,10 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   } else if (gu) {
     if (a->out_dtype == MOE_DT_F32) return MOE_ERR_INVALID_ARG;
     if (a->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-    if (q4 ? a->out_dtype != MOE_DT_F16 : (a->wfmt != MOE_W_DENSE_NK && !w8)) return MOE_ERR_UNSUPPORTED;
+    if (q4 ? a->out_dtype != MOE_DT_F16 : (a->wfmt == MOE_W_DENSE_NK_F16)) return MOE_ERR_UNSUPPORTED;
   } else {
     if (a->out_dtype != MOE_DT_F32 && a->out_dtype != a->act_dtype) return MOE_ERR_INVALID_ARG;
-    if (!w8 && (a->act_dtype == MOE_DT_BF16 ? a->wfmt != MOE_W_DENSE_NK
+    if (!w8 && (a->act_dtype == MOE_DT_BF16 ? (a->wfmt != MOE_W_DENSE_NK && a->wfmt != MOE_W_DENSE)
                                             : (a->wfmt != MOE_W_DENSE_NK_F16 && !q4)))
       return MOE_ERR_UNSUPPORTED;
   }
@@ -182,7 +182,8 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   const long long esz = a->act_dtype == MOE_DT_F32 ? 4 : 2;
   if ((long long)a->a_rows * a->K * esz >= (1LL << 31) || (long long)a->K * a->N * (w8 ? 1 : esz) >= (1LL << 32))
     return MOE_ERR_UNSUPPORTED;
-  if (q4 && (a->group_size < 8 || a->group_size % 8 != 0 || a->K % a->group_size != 0))
+  if (q4 && (a->group_size < 8 || (a->group_size % 64 != 0 && 64 % a->group_size != 0) ||
+             a->K % a->group_size != 0))
     return MOE_ERR_UNSUPPORTED;
   return enqueue([&] { return moe::launch_grouped_gemm(*a, as_stream(stream)); });
 }

@@ -164,10 +164,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // projection over an fp32 weight split into two bf16 planes.
 // W8_: fp8 (e4m3) weights [e][N][K], converted exactly to the operand type (bf16 or fp16) on their
 // way to LDS, with one scale per output column applied in the epilogue.
+// KN_: dense bf16 weights in the stated [e][K][N] layout (each K row's N weights contiguous): K
+// rows go to LDS as they are and the MFMA B operands are read transposed (ds_read_b64_tr_b16).
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GU_, bool Q4_, int WGS_ = 1, int REGSETS_ = 2,
-          bool F16_ = Q4_, bool ACVT_ = false, bool SUM_ = false, bool W8_ = false>
+          bool F16_ = Q4_, bool ACVT_ = false, bool SUM_ = false, bool W8_ = false, bool KN_ = false>
 struct Cfg {
-  static constexpr bool F16 = F16_, ACVT = ACVT_, SUM = SUM_, W8 = W8_;
+  static constexpr bool F16 = F16_, ACVT = ACVT_, SUM = SUM_, W8 = W8_, KN = KN_;
   // fp16 operands carry weights scaled by 2^8 (int4, prepared dense fp16), fp8 ones do not
   static constexpr float OUT_MUL = (F16_ && !W8_) ? 1.0f / kF16WeightScale : 1.0f;
   // Chunks held in registers between their loads and their LDS stores (two LDS buffers only).
@@ -195,7 +197,7 @@ struct Cfg {
   static constexpr int NTL = BN / WN / 16;          // 16-column MFMA tiles per wave and matrix
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves");
   static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
-  static_assert(REGSETS == 2 || (REGSETS == 1 && STAGES == 2), "register sets");
+  static_assert(REGSETS == 2 || (REGSETS == 1 && STAGES == 2) || (REGSETS == 4 && STAGES == 1), "register sets");
   static_assert(A_CHUNKS % NT == 0 || NT % A_CHUNKS == 0, "A tile split");
   static_assert(B_UNITS >= 1 && (NW * KC * BN) % (32 * NT) == 0, "B tile split");
   static_assert(MT >= 1 && NTL >= 1, "wave tile");
@@ -205,6 +207,7 @@ struct Cfg {
   static_assert(!ACVT || F16, "activations are converted to the fp16 operand type");
   static_assert(!SUM || (GU && !Q4 && !F16 && !W8_), "router sums: two dense bf16 weight planes");
   static_assert(!(Q4 && W8_), "one weight format");
+  static_assert(!KN_ || (!Q4 && !W8_ && !F16 && (BN == 64 || BN == 128)), "[K][N] tiles: bf16, 64 or 128 columns");
   static size_t lds_bytes(int n_groups) { return STAGES * STAGE * 2 + 2 * sizeof(int) * (n_groups + 1) + 16; }
 };
 
@@ -216,6 +219,17 @@ struct Cfg {
 // offsets.  Dequantised int4 columns are written so that each 16-lane pass fills 8 chunks of an
 // even row and 8 of an odd row (see the int4 unit mapping), also without conflicts.
 __device__ __forceinline__ int lds_off_rows(int n, int q) { return n * 64 + ((q ^ ((n >> 1) & 7)) << 3); }
+
+// [K][N] weight tiles hold one row of BN columns per k (BN / 8 chunks of 16 bytes); chunk c of row
+// k sits at position c ^ swz_kn(k).  A transposed operand read by 32 lanes touches 8 rows (k and
+// k + 8 blocks of 4) and 2 chunks in each; swz_kn sends them to 16 different 16-byte bank slots
+// (rows of 256 bytes fill all 64 banks, rows of 128 bytes half of them, alternating).  Within a
+// lane's operand reads swz_kn depends only on the lane, so each read is one base plus offsets.
+template <int BN>
+__device__ __forceinline__ int swz_kn(int k) {
+  if constexpr (BN == 128) return 2 * ((k & 3) + 4 * ((k >> 3) & 1));
+  else return 2 * (((k >> 1) & 1) + 2 * ((k >> 3) & 1));
+}
 
 // Registers holding one K chunk in flight: the activation rows and the weight units of this
 // thread.
@@ -248,10 +262,13 @@ struct TileCtx {
   int b_lds;                                        // dense: LDS destination of the lane's first piece
   uint32_t b_off[C::B_UNITS];                       // int4: word offset of the unit
   uint32_t s_off[C::B_UNITS];                       // int4: scale offset of the unit
+  uint32_t kn_voff[C::KN ? C::B_PIECES : 1];        // [K][N]: lane offset of each 16-byte piece (row k, chunk c)
+  int kn_dst[C::KN ? C::B_PIECES : 1];              // [K][N]: LDS destination of each piece
+  int kn_m[C::KN ? C::B_PIECES : 1];                // [K][N]: matrix of each piece (wave-uniform)
+  uint32_t kn_soff;                                 // [K][N]: byte offset of the tile's first column
   int b_dst[C::B_UNITS][(C::Q4 || C::W8) ? 4 : 1];  // int4: LDS destination of each dequantised column;
                                                     // fp8: of each 16-byte chunk of the unit
   bool b_swap[C::B_UNITS];                          // int4: columns written in swapped pairs
-  int b_k[C::B_UNITS];                              // int4: first k of the unit's word row in a chunk
   const u16* es[C::NW];                             // fp8: scales of the tile's first column, per matrix
   int nK, row_bytes, s_row_bytes, group_size;
 };
@@ -269,6 +286,17 @@ __device__ __forceinline__ void load_a(const TileCtx<C>& t, int kc, AChunk<C>& c
 template <class C>
 __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& ch) {
   kc = min(kc, t.nK - 1);
+  if constexpr (C::KN) {
+    // [K][N]: piece x is 8 consecutive columns of one K row of the chunk
+    const uint32_t so = t.kn_soff + (uint32_t)kc * C::KC * t.row_bytes;
+#pragma unroll
+    for (int x = 0; x < C::B_PIECES; ++x) {
+      __amdgpu_buffer_rsrc_t w = t.wr[0];
+      if constexpr (C::NW == 2) w = t.kn_m[x] ? t.wr[1] : t.wr[0];
+      ch.b[x / C::R][x % C::R] = __builtin_amdgcn_raw_buffer_load_b128(w, t.kn_voff[x], so, 2);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (C::W8) {
@@ -288,8 +316,10 @@ __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& c
     } else {
       ch.b[i][0] = __builtin_amdgcn_raw_buffer_load_b128(
           t.wr[i], t.b_off[i] + (uint32_t)(kc * (C::KC / 8)) * t.row_bytes, 0, 2);
-      // the scale group of this unit's word row (groups of 8 k or more: one per word at least)
-      const int grp = (kc * C::KC + t.b_k[i]) / t.group_size;
+      // the scale group of this unit's word row, (kc * 64 + k) / group_size: the chunk's first
+      // group (kc * 64) / group_size, exact for group sizes that divide 64 or are multiples of it,
+      // plus the word row's group inside the chunk (nonzero below 64), which s_off holds
+      const int grp = (kc * C::KC) / t.group_size;
       ch.s[i] = __builtin_amdgcn_raw_buffer_load_b64(t.sr[i], t.s_off[i] + (uint32_t)grp * t.s_row_bytes, 0, 0);
     }
   }
@@ -357,6 +387,11 @@ __device__ __forceinline__ u32x2 fp8x4_to_16(uint32_t d) {
 template <class C>
 __device__ __forceinline__ void store_w(const TileCtx<C>& t, const WChunk<C>& ch, u16* buf) {
   u16* sB = buf + C::A_ELEMS;
+  if constexpr (C::KN) {
+#pragma unroll
+    for (int x = 0; x < C::B_PIECES; ++x) *reinterpret_cast<u32x4*>(sB + t.kn_dst[x]) = ch.b[x / C::R][x % C::R];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (C::W8) {
@@ -395,6 +430,26 @@ __device__ __forceinline__ void store_chunk(const TileCtx<C>& t, const Chunk<C>&
   store_w(t, ch.w, buf);
 }
 
+// B operand of one 16x16x32 MFMA from a [K][N] tile: lanes 16 g .. 16 g + 15 need k = ks + 8 g ..
+// + 7 of columns ncol .. ncol + 15.  ds_read_b64_tr_b16 gives lane i of a 16-lane group the
+// (i % 4)-th 16-bit value of the 8 bytes addressed by lane 4 j + i / 4 as its value j, so lane L
+// addresses columns ncol + 4 (L % 4) .. + 3 of row k0 + L / 4; two reads cover k0 = 8 g and 8 g + 4.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+template <class C>
+__device__ __forceinline__ u32x4 read_kn_operand(const u16* sB, int m, int ks, int ncol) {
+  const int lane = threadIdx.x & 63, L = lane & 15, g = lane >> 4;
+  const int k = ks + 8 * g + (L >> 2);
+  const int c = (ncol >> 3) + ((L & 3) >> 1);
+  const int off = m * C::BN * C::KC + k * C::BN + ((c ^ swz_kn<C::BN>(k)) << 3) + 4 * (L & 1);
+  const bf16x4_t* p0 = reinterpret_cast<const bf16x4_t*>(sB + off);
+  const bf16x4_t* p1 = reinterpret_cast<const bf16x4_t*>(sB + off + 4 * C::BN);   // k + 4 (same swizzle)
+  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+  const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+  const u32x2 a = __builtin_bit_cast(u32x2, v0), b = __builtin_bit_cast(u32x2, v1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // MFMAs of one LDS chunk for the NM live 16-row tiles of this wave (tile i covers rows
 // arow0 - lane%16 + 16 * WM * i: the 16-row tiles of a workgroup tile are dealt to its WM wave
 // rows in turn, which balances partially filled tiles).
@@ -416,8 +471,13 @@ __device__ __forceinline__ void compute_chunk(const u16* buf, f32x4 (&acc)[C::NW
       for (int m = 0; m < C::NW; ++m) {
 #pragma unroll
         for (int j = 0; j < C::NTL; ++j) {
-          const int off = lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64;
-          const u32x4 bv = *reinterpret_cast<const u32x4*>(sB + off);
+          u32x4 bv;
+          if constexpr (C::KN) {
+            bv = read_kn_operand<C>(sB, m, ks, bcol - (bcol & 15) + j * 16);
+          } else {
+            const int off = lds_off_rows(bcol, (ks + kofs) >> 3) + (m * C::BN + j * 16) * 64;
+            bv = *reinterpret_cast<const u32x4*>(sB + off);
+          }
 #pragma unroll
           for (int i = 0; i < NM; ++i) acc[m][i][j] = mma<C::F16>(av[i], bv, acc[m][i][j]);
         }
@@ -486,6 +546,23 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
       __syncthreads();
     }
     if (kc < nK) compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+  } else if constexpr (C::REGSETS == 4) {
+    // One LDS buffer, four chunks in registers (the caller keeps K a multiple of 4 chunks): the
+    // quantised weights carry half or a quarter of the bytes of a 16-bit chunk, so a
+    // decode-shaped tile keeps twice as many chunks in flight to hold the same bytes in flight.
+    Chunk<C> c[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_chunk(t, r, c[r]);
+    for (; kc < nK; kc += 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        store_chunk(t, c[r], buf0);
+        __syncthreads();
+        compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
+        load_chunk(t, kc + 4 + r, c[r]);                 // clamped past the end
+        __syncthreads();
+      }
+    }
   } else {
     Chunk<C> c0, c1;
     load_chunk(t, 0, c0);
@@ -601,7 +678,26 @@ void k_gemm_bf16(GemmParams p) {
     }
     // piece i of a thread lands SLICE_ROWS * i rows below piece 0 (the swizzle repeats every 16 rows)
     t.a_lds = lds_off_rows((tid % C::A_CHUNKS) / (KC / 8), tid % (KC / 8));
-    if constexpr (C::W8) {
+    if constexpr (C::KN) {
+      // [K][N]: piece p of a matrix's chunk is row p / (BN / 8), 8 columns at chunk p % (BN / 8);
+      // 16 (BN = 128) or 8 (BN = 64) lanes read one 256- or 128-byte row
+      constexpr int per_m = KC * BN / 8;
+      static_assert(per_m % 64 == 0, "a wave's pieces read one matrix");
+#pragma unroll
+      for (int m = 0; m < C::NW; ++m)
+        t.wr[m] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)e * w_bytes, w_bytes);
+#pragma unroll
+      for (int x = 0; x < C::B_PIECES; ++x) {
+        const int pidx = tid + NT * x;
+        const int m = __builtin_amdgcn_readfirstlane(pidx / per_m);
+        const int q = pidx % per_m, k = q / (BN / 8), c = q % (BN / 8);
+        t.kn_m[x] = m;
+        t.kn_voff[x] = (uint32_t)((k * p.N + c * 8) * 2);
+        t.kn_dst[x] = m * BN * KC + k * BN + ((c ^ swz_kn<BN>(k)) << 3);
+      }
+      t.kn_soff = (uint32_t)n0 * 2;
+      t.row_bytes = p.N * 2;
+    } else if constexpr (C::W8) {
       // fp8 [e][n][k]: unit u of a matrix covers k = 32 (u % 2) .. + 31 of column u / 2, so two
       // lanes read one column's 64 bytes of a chunk; each 16-lane LDS pass writes 8 columns (4
       // even, 4 odd rows) at two chunk positions each, one per bank group.
@@ -654,9 +750,10 @@ void k_gemm_bf16(GemmParams p) {
         const int m = (tid + NT * i) / per_m;
         const int sw = nq & 1;
         t.b_off[i] = (uint32_t)(kw * p.N + n0 + nq * 4) * 4u;
-        t.s_off[i] = (uint32_t)(n0 + nq * 4) * 2u;
+        // scale row of the word row's group inside a chunk (group sizes below 64)
+        const int kg = p.group_size < KC ? kw * 8 / p.group_size : 0;
+        t.s_off[i] = (uint32_t)(kg * p.N + n0 + nq * 4) * 2u;
         t.b_swap[i] = sw != 0;
-        t.b_k[i] = kw * 8;
 #pragma unroll
         for (int c = 0; c < 4; ++c) t.b_dst[i][c] = lds_off_rows(m * BN + nq * 4 + (c ^ sw), kw);
       }
@@ -1350,7 +1447,7 @@ hipError_t run_bf16(const GemmParams& p, int wgs_per_cu, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   grid = ((grid + 7) / 8) * 8;
   if (grid < 8) grid = 8;
-  if constexpr (C::STAGES == 1 && !C::Q4 && !C::SUM && !C::W8) {
+  if constexpr (C::STAGES == 1 && !C::Q4 && !C::SUM && !C::W8 && !C::KN) {
     if (p.row_index == nullptr && (p.K / C::KC) % 2 == 0) {
       k_gemm_stream<C, OutT><<<dim3((unsigned)grid), dim3(C::NT), lds, s>>>(p);
       return hipGetLastError();
@@ -1482,18 +1579,38 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   const bool h16 = a.out_dtype == MOE_DT_F16;
   // The ABI guarantees N % 64 == 0 (gate/up) and N % 128 == 0 (down): variants 0 and 2 always fit.
   const bool small_m = a.m_hint > 0 && a.m_hint <= 48;   // decode-shaped: weight streaming
+  const bool k4 = p.K % 256 == 0;                       // four 64-k chunks per register round
+  if (a.wfmt == MOE_W_DENSE) {
+    // bf16 weights in the stated [e][K][N] layout: register-staged tiles with transposed operand
+    // reads (the prepared [e][N][K] copy takes the faster paths below)
+    if (gu) {
+      if (small_m) return h16 ? run_bf16<Cfg<32, 64, 1, 4, 1, true, false, 4, 2, false, false, false, false, true>, _Float16>(p, 4, s)
+                              : run_bf16<Cfg<32, 64, 1, 4, 1, true, false, 4, 2, false, false, false, false, true>, u16>(p, 4, s);
+      return h16 ? run_bf16<Cfg<256, 64, 4, 1, 2, true, false, 1, 2, false, false, false, false, true>, _Float16>(p, 1, s)
+                 : run_bf16<Cfg<256, 64, 4, 1, 2, true, false, 1, 2, false, false, false, false, true>, u16>(p, 1, s);
+    }
+    if (small_m) return f32out ? run_bf16<Cfg<32, 128, 1, 4, 1, false, false, 2, 2, false, false, false, false, true>, float>(p, 2, s)
+                               : run_bf16<Cfg<32, 128, 1, 4, 1, false, false, 2, 2, false, false, false, false, true>, u16>(p, 2, s);
+    return f32out ? run_bf16<Cfg<256, 128, 4, 1, 2, false, false, 1, 2, false, false, false, false, true>, float>(p, 1, s)
+                  : run_bf16<Cfg<256, 128, 4, 1, 2, false, false, 1, 2, false, false, false, false, true>, u16>(p, 1, s);
+  }
   if (a.wfmt == MOE_W_FP8_E4M3) {
     if (gu) {
-      if (small_m) return run_gu_w8<32, 64, 1, 4, 1, 4, 2>(p, h16, s);
+      if (small_m) return k4 ? run_gu_w8<32, 64, 1, 4, 1, 4, 4>(p, h16, s) : run_gu_w8<32, 64, 1, 4, 1, 4, 2>(p, h16, s);
       if (p.N % 128 == 0) return run_gu_w8<192, 128, 4, 2, 2, 1, 1>(p, h16, s);
       return run_gu_w8<256, 64, 4, 1, 2, 1, 2>(p, h16, s);
     }
-    if (small_m) return run_dn_w8<32, 128, 1, 4, 1, 4, 2>(p, f16, f32out, s);
-    // 4-wave 256 x 128 tiles: the 8-wave 256 x 256 tile needs more than two waves' registers
+    if (small_m)
+      return k4 ? run_dn_w8<32, 128, 1, 4, 1, 4, 4>(p, f16, f32out, s) : run_dn_w8<32, 128, 1, 4, 1, 4, 2>(p, f16, f32out, s);
+    // 8-wave 192 x 256 tiles (256 rows need more than two waves' registers per SIMD)
+    if (p.N % 256 == 0) return run_dn_w8<192, 256, 4, 2, 2, 1, 1>(p, f16, f32out, s);
     return run_dn_w8<256, 128, 4, 1, 2, 1, 2>(p, f16, f32out, s);
   }
   if (gu) {
-    if (small_m) return run_gu<32, 64, 1, 4, 1, 4, 2>(p, q4, h16, s);
+    if (small_m) {
+      if (q4 && k4) return run_gu_q4<32, 64, 1, 4, 1, 4, 4>(p, s);
+      return run_gu<32, 64, 1, 4, 1, 4, 2>(p, q4, h16, s);
+    }
     if (p.N % 128 == 0) {
       // int4: 192-row tiles (256 rows need more than the 256 registers of two waves per SIMD)
       if (q4) return run_gu_q4<192, 128, 4, 2, 2, 1, 1>(p, s);
@@ -1504,11 +1621,17 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
   if (small_m) {
     // dense: two workgroups per CU (half as many weight streams, each workgroup streams several
     // tiles back to back): 2 % faster than four on the decode-shaped down projection
-    if (q4) return run_dn<32, 128, 1, 4, 1, 4, 2>(p, q4, f16, f32out, s);
+    if (q4) {
+      if (k4) return f32out ? run_cfg_dn<32, 128, 1, 4, 1, 4, 4, true, true, float>(p, s)
+                            : run_cfg_dn<32, 128, 1, 4, 1, 4, 4, true, true, _Float16>(p, s);
+      return run_dn<32, 128, 1, 4, 1, 4, 2>(p, q4, f16, f32out, s);
+    }
     return run_dn<32, 128, 1, 4, 1, 2, 2>(p, q4, f16, f32out, s);
   }
   if (p.N % 256 != 0) return run_dn<256, 128, 4, 1, 2, 1, 2>(p, q4, f16, f32out, s);
-  if (q4) return run_dn<256, 256, 4, 2, 2, 1, 1>(p, q4, f16, f32out, s);
+  // int4: 192-row tiles (the 256-row tile sits at the 256 registers of two waves per SIMD)
+  if (q4) return f32out ? run_cfg_dn<192, 256, 4, 2, 2, 1, 1, true, true, float>(p, s)
+                        : run_cfg_dn<192, 256, 4, 2, 2, 1, 1, true, true, _Float16>(p, s);
   if (f16) return f32out ? run_dma_dn<true, float>(p, s) : run_dma_dn<true, _Float16>(p, s);
   return f32out ? run_dma_dn<false, float>(p, s) : run_dma_dn<false, u16>(p, s);
 }

@@ -35,6 +35,7 @@ class ExpertWeights:
     shared_down: torch.Tensor | None = None
 
     h_fp8: torch.dtype = torch.float16   # h's dtype over fp8 down weights (fp16 or bf16)
+    stated_layout: bool = False          # dense bf16 weights left [e][K][N] (no preparation)
 
     @property
     def int4(self) -> bool:
@@ -60,7 +61,8 @@ def _t(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def upload(inputs: dict, cfg, device="cuda", h_dtype=torch.float16) -> tuple[torch.Tensor, torch.Tensor, ExpertWeights]:
+def upload(inputs: dict, cfg, device="cuda", h_dtype=torch.float16,
+           stated_layout: bool = False) -> tuple[torch.Tensor, torch.Tensor, ExpertWeights]:
     """Copy a workloads.make_inputs() dict to the GPU -> (x, logits, weights).  Dense weights
     arrive [E][K][N] and are prepared once by the library: gate/up with moe_prepare_dense_weights,
     the down projections of a bf16 layer with moe_prepare_dense_weights_f16 when h_dtype is fp16
@@ -68,6 +70,12 @@ def upload(inputs: dict, cfg, device="cuda", h_dtype=torch.float16) -> tuple[tor
     x = _t(inputs["x"], device)
     logits = _t(inputs["logits"], device)
     assert h_dtype in (torch.float16, torch.bfloat16)
+    if stated_layout:
+        # dense bf16 weights as the layer states them, [e][K][N] (MOE_W_DENSE): the grouped GEMM
+        # reads their K rows and transposes its operands; h is bf16 (down weights stay bf16)
+        assert cfg.wfmt == "dense" and cfg.act == "bf16" and not cfg.shared_I
+        return x, logits, ExpertWeights(w_gate=_t(inputs["w_gate"], device), w_up=_t(inputs["w_up"], device),
+                                        w_down=_t(inputs["w_down"], device), stated_layout=True)
 
     def dense(name):
         return ops.prepare_dense_weights(_t(inputs[name], device))
@@ -139,6 +147,8 @@ class MoELayer:
                              "prepare_dense_weights_f16")
         if W.int4:
             want = {"w_gate": (el, H // 8, I), "w_up": (el, H // 8, I), "w_down": (el, I // 8, H)}
+        elif W.stated_layout:
+            want = {"w_gate": (el, H, I), "w_up": (el, H, I), "w_down": (el, I, H)}
         elif W.fp8:
             want = {"w_gate": (el, I, H), "w_up": (el, I, H), "w_down": (el, H, I),
                     "s_gate": (el, I), "s_up": (el, I), "s_down": (el, H)}
@@ -194,13 +204,13 @@ class MoELayer:
         ops.grouped_gemm(_abi.MOE_OP_GATE_UP_SWIGLU, x, b.group_offsets, W.w_gate, W.w_up, b.h,
                          K=self.H, N=self.I, row_index=b.sorted_pairs, row_div=self.k, s0=W.s_gate,
                          s1=W.s_up, group_size=W.group_size or self.H, m_hint=self.m_hint(x.shape[0]),
-                         stream=stream)
+                         weights_nk=not W.stated_layout, stream=stream)
 
     def step_down(self, x, b, stream=None):
         W = self.weights
         ops.grouped_gemm(_abi.MOE_OP_DOWN, b.h, b.group_offsets, W.w_down, None, b.o, K=self.I, N=self.H,
                          s0=W.s_down, group_size=W.group_size or self.I, m_hint=self.m_hint(x.shape[0]),
-                         stream=stream)
+                         weights_nk=not W.stated_layout, stream=stream)
 
     def step_shared(self, x, b, stream=None):
         W, T = self.weights, x.shape[0]

@@ -70,6 +70,10 @@ CONFIGS = {
                               wfmt="int4", group_size=128),
     "w4a16_channel": MoEConfig("w4a16_channel", T=8192, H=4096, E=512, k=10, I=1024, e_first=0,
                                e_local=64, wfmt="int4", group_size=0),
+    # Skewed routing plus the shared expert with int4 routed experts: hot experts of up to 8192
+    # rows, where the matrix units bind (the high end of the bf16 / W4A16 comparison).
+    "w4a16_skewed": MoEConfig("w4a16_skewed", T=8192, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
+                              shared_I=1024, zipf_bias=2.0, wfmt="int4", group_size=128),
     # Decode and prefill shapes with FP8 (e4m3) expert weights, one bf16 scale per output channel.
     "fp8_decode": MoEConfig("fp8_decode", T=512, H=4096, E=512, k=10, I=1024, e_first=0, e_local=64,
                             wfmt="fp8"),

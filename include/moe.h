@@ -58,7 +58,7 @@ typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_F16 = 2 } moe_d
 /* Expert weight formats for a K x N matrix W of expert e (output n = sum_k a[k] W[k][n]).
  * MOE_W_DENSE: W[e][k][n] in the activation dtype, the layout the layer is stated in.
  * MOE_W_DENSE_NK: the same values stored [e][n][k] (row n = the K weights of output n), as
- * moe_prepare_dense_weights writes them; the bf16 grouped GEMM reads this layout.
+ * moe_prepare_dense_weights writes them; the bf16 grouped GEMM's fastest tiles read this layout.
  * MOE_W_DENSE_NK_F16: fp16 [e][n][k] holding 2^8 * W (moe_prepare_dense_weights_f16 writes it
  * from bf16 MOE_W_DENSE weights), the weights of a down projection over fp16 h.  The conversion
  * is exact for 2^-22 <= |W| <= 255 (fp16's normal range shifted by 2^8); smaller magnitudes keep
@@ -217,16 +217,18 @@ moe_status moe_permute_noalloc(const int32_t* blob, int T, int k, int e_first, i
  * A row a[row_index[r] / row_div] (or a[r] when row_index is NULL) and expert e's weights.
  * GATE_UP_SWIGLU: out[r][n] = silu(sum_k A[k] Wg(e)[k][n]) * (sum_k A[k] Wu(e)[k][n]).
  * DOWN:           out[r][n] = sum_k A[k] Wd(e)[k][n].
- * Supported combinations (anything else is MOE_ERR_UNSUPPORTED; MOE_W_DENSE with 16-bit
- * activations is prepared once with moe_prepare_dense_weights[_f16]):
+ * Supported combinations (anything else is MOE_ERR_UNSUPPORTED):
  *   fp32:     a, weights (MOE_W_DENSE or MOE_W_DENSE_NK) and out fp32; vector-ALU fp32 arithmetic.
- *   GATE_UP:  a = x bf16; MOE_W_DENSE_NK bf16 or MOE_W_FP8_E4M3 weights (bf16 MFMA operands) with
- *             out (h) bf16 or fp16, or MOE_W_INT4_SYM_GROUP with out fp16.
- *   DOWN:     a = h bf16 with MOE_W_DENSE_NK bf16 weights (bf16 operands), or a = h fp16 with
+ *   GATE_UP:  a = x bf16; MOE_W_DENSE or MOE_W_DENSE_NK bf16 or MOE_W_FP8_E4M3 weights (bf16 MFMA
+ *             operands) with out (h) bf16 or fp16, or MOE_W_INT4_SYM_GROUP with out fp16.
+ *   DOWN:     a = h bf16 with MOE_W_DENSE or MOE_W_DENSE_NK bf16 weights (bf16 operands), or a = h fp16 with
  *             MOE_W_DENSE_NK_F16 or MOE_W_INT4_SYM_GROUP weights (fp16 operands), or a = h bf16 or
  *             fp16 with MOE_W_FP8_E4M3 weights (operands in h's dtype); out fp32 or a's dtype.
  * fp8 weights convert exactly to bf16 and to fp16 (4 significant bits; exponents 2^-9..2^8) on
  * their way to LDS; their per-column scales multiply the fp32 accumulators in the epilogue.
+ * Bf16 weights in the stated MOE_W_DENSE [e][K][N] layout are read as they are (K rows staged in
+ * LDS, operands read transposed; same results, bit for bit, as MOE_W_DENSE_NK); the prepared
+ * MOE_W_DENSE_NK copy (moe_prepare_dense_weights) takes the faster tile paths.
  * Accumulation is fp32 throughout.  int4 weights run on fp16 operands: each weight q * s is
  * dequantised exactly to fp16 in LDS (q * s has at most 11 significant bits, which bf16 would
  * round), as 2^8 * q * s, exact for scales 2^-22 <= s < 32; their bf16 activations x are converted
@@ -241,8 +243,8 @@ typedef struct moe_gemm_args {
   int32_t op;          /* moe_gemm_op */
   int32_t act_dtype;   /* moe_dtype of a (and of dense MOE_W_DENSE / MOE_W_DENSE_NK weights) */
   int32_t wfmt;        /* moe_wfmt of w0 / w1 (int4 requires MOE_DT_BF16) */
-  int32_t group_size;  /* int4: K rows per scale; a multiple of 8 that divides K (K: channel-wise).
-                          fp8: K.  Dense: 0 */
+  int32_t group_size;  /* int4: K rows per scale, dividing K: 8, 16, 32 or a multiple of 64
+                          (K: channel-wise).  fp8: K.  Dense: 0 */
   int32_t K;           /* contraction length: H for GATE_UP, I for DOWN; multiple of 64 */
   int32_t N;           /* output columns: I for GATE_UP (multiple of 64), H for DOWN (multiple
                           of 128) */

@@ -130,7 +130,7 @@ def _gemm(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(op=2), INV), (dict(act_dtype=7), UNS), (dict(wfmt=5), UNS), (dict(out_dtype=0), INV),
-    (dict(wfmt=0), UNS),                      # bf16 GEMM reads prepared (MOE_W_DENSE_NK) weights
+    (dict(wfmt=0, act_dtype=1, out_dtype=0), INV),       # gate/up never writes fp32 from bf16
     (dict(out_dtype=4), UNS), (dict(act_dtype=0, out_dtype=1), INV),
     (dict(a=None), INV), (dict(group_offsets=None), INV), (dict(w0=None), INV), (dict(out=None), INV),
     (dict(w1=None), INV), (dict(op=1, K=128, N=256, w1=FAKE), INV), (dict(K=32), INV), (dict(K=96), INV),
@@ -141,6 +141,7 @@ def _gemm(**kw):
     (dict(wfmt=1, out_dtype=2, group_size=20, s0=FAKE, s1=FAKE), UNS),      # not whole words
     (dict(wfmt=1, out_dtype=2, group_size=4, s0=FAKE, s1=FAKE), UNS),
     (dict(wfmt=1, out_dtype=2, group_size=96, s0=FAKE, s1=FAKE), UNS),      # does not divide K
+    (dict(wfmt=1, out_dtype=2, K=192, group_size=48, s0=FAKE, s1=FAKE), UNS),   # neither divides nor is a multiple of 64
     (dict(wfmt=1, out_dtype=2, K=192, group_size=128, s0=FAKE, s1=FAKE), UNS),
     # int4 runs on fp16 operands: gate/up writes fp16 h, down reads fp16 h
     (dict(wfmt=1, out_dtype=1, group_size=128, s0=FAKE, s1=FAKE), UNS),
@@ -148,6 +149,7 @@ def _gemm(**kw):
     # fp16 h over fp16 weights, bf16 h over bf16 weights; no fp16 gate/up input
     (dict(op=1, K=128, N=256, w1=None, wfmt=3, act_dtype=1, out_dtype=0), UNS),
     (dict(op=1, K=128, N=256, w1=None, wfmt=2, act_dtype=2, out_dtype=0), UNS),
+    (dict(op=1, K=128, N=256, w1=None, wfmt=0, act_dtype=2, out_dtype=0), UNS),   # [K][N] weights are bf16
     (dict(op=1, K=128, N=256, w1=None, wfmt=3, act_dtype=2, out_dtype=1), INV),
     (dict(act_dtype=2, out_dtype=2), UNS), (dict(wfmt=3, out_dtype=2), UNS),
     (dict(act_dtype=0, out_dtype=0, wfmt=3), UNS),

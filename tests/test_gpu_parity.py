@@ -348,6 +348,56 @@ def test_down_projection_16bit_output_and_16bit_combine(name, h_dtype, hint):
     _check_close(_np(y).astype(np.float64), ref, f"{name} h {h_dtype} 16-bit o")
 
 
+@pytest.mark.parametrize("hint", [8, 1 << 20], ids=["decode_tiles", "prefill_tiles"])
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_skew_empty", "bf16_all_local_k1",
+                                  "bf16_many_tiles_per_workgroup", "bf16_80_local_experts"])
+def test_stated_layout_weights_equal_the_prepared_layout(name, hint):
+    """Dense bf16 weights in the stated [e][K][N] layout (MOE_W_DENSE, transposed operand reads)
+    give the same bits as the prepared [e][N][K] copy (the same products in the same order) for
+    gate/up with bf16 and fp16 h and for the down projection over bf16 h, on both tile families;
+    the layer on them matches the oracle."""
+    cfg = MID[name]
+    inp = W.make_inputs(cfg)
+    x, logits, kn = upload(inp, cfg, _dev(), stated_layout=True)
+    _, _, nk = upload(inp, cfg, _dev(), h_dtype=torch.bfloat16)
+    layer = MoELayer.from_config(cfg, kn)
+    layer.m_hint = lambda T: hint
+    y = layer.forward(x, logits)
+    b = layer.buffers(cfg.T, x.device)
+    assert b.h.dtype == torch.bfloat16
+    n = b.group_offsets[-1]
+    for h_dtype in (torch.bfloat16, torch.float16):
+        h1 = torch.empty(b.h.shape, dtype=h_dtype, device=x.device)
+        h2 = torch.empty_like(h1)
+        ops.grouped_gemm(0, x, b.group_offsets, kn.w_gate, kn.w_up, h1, K=cfg.H, N=cfg.I, row_index=b.sorted_pairs,
+                         row_div=cfg.k, m_hint=hint, weights_nk=False)
+        ops.grouped_gemm(0, x, b.group_offsets, nk.w_gate, nk.w_up, h2, K=cfg.H, N=cfg.I, row_index=b.sorted_pairs,
+                         row_div=cfg.k, m_hint=hint)
+        torch.cuda.synchronize()
+        assert torch.equal(h1[:n].view(torch.int16), h2[:n].view(torch.int16))
+    o1 = torch.empty((b.h.shape[0], cfg.H), dtype=torch.float32, device=x.device)
+    o2 = torch.empty_like(o1)
+    ops.grouped_gemm(1, b.h, b.group_offsets, kn.w_down, None, o1, K=cfg.I, N=cfg.H, m_hint=hint, weights_nk=False)
+    ops.grouped_gemm(1, b.h, b.group_offsets, nk.w_down, None, o2, K=cfg.I, N=cfg.H, m_hint=hint)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:n].view(torch.int32), o2[:n].view(torch.int32))
+    ids, w = oracle.route(inp["logits"], cfg.k)
+    _check_close(_np(y).astype(np.float64), oracle.layer(inp, cfg, ids, w, threads=8), f"{name} stated layout")
+
+
+def test_stated_layout_full_decode_every_token():
+    """The decode workload with its weights in the stated [e][K][N] layout, every token."""
+    cfg = W.CONFIGS["decode"]
+    inp = W.make_inputs(cfg, threads=16)
+    x, logits, kn = upload(inp, cfg, _dev(), stated_layout=True)
+    layer = MoELayer.from_config(cfg, kn)
+    y = layer.forward(x, logits)
+    torch.cuda.synchronize()
+    ids, w, off = _check_routing(layer.buffers(cfg.T, x.device), inp, cfg)
+    _check_close(_np(y).astype(np.float64), oracle.layer(inp, cfg, ids, w, threads=ORACLE_THREADS),
+                 "decode stated layout all 512 tokens")
+
+
 def test_layer_single_token_and_single_expert():
     cfg = W.MoEConfig("one", T=1, H=128, E=4, k=2, I=64, e_first=1, e_local=1)
     inp = W.make_inputs(cfg)
@@ -435,6 +485,20 @@ def test_layer_skewed_shared_every_token(skewed_run, part):
         print("skewed_shared n_loc", int(off[-1]), "empty groups", int((sizes == 0).sum()),
               "max group", int(sizes.max()), "experts with > 4 m-tiles of 256 rows", int((sizes > 1024).sum()))
         assert (sizes > 4 * 256).sum() >= 1        # the grouped-M order past its first group runs
+
+
+def test_layer_int4_skewed_shared_first_quarter():
+    """int4 routed experts under the skewed routing (hot experts of up to 8192 rows on the
+    192-row int4 tiles, empty experts) plus the dense shared expert: the first 2048 tokens on
+    both tile families."""
+    cfg = W.CONFIGS["w4a16_skewed"]
+    inp = W.make_inputs(cfg, threads=16)
+    ids, w, off, ys = _both_families(cfg, inp)
+    toks = np.arange(cfg.T // 4, dtype=np.int32)
+    ref = oracle.layer(inp, cfg, ids, w, tokens=toks, threads=ORACLE_THREADS)
+    for fam, yn in ys.items():
+        _check_close(yn[toks], ref, f"w4a16_skewed/{fam} tokens 0..{toks[-1]}")
+    assert np.all(np.isfinite(ys["prefill_tiles"]))
 
 
 # ----------------------------------------------------------------------------------------------
