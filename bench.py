@@ -497,6 +497,14 @@ def main():
         "attainable": att,
         "workloads": {head: {k: v for k, v in h.items() if k not in ("workload",)}, **subs},
     }
+    # bf16 vs W4A16 expert weights on the same routing (the weight-format rule's measurements)
+    wl = out["workloads"]
+    out["format_rule"] = {
+        f"{a}/{b}": {"rows_per_expert": round(wl[a]["n_local_pairs"] / wl[a]["config"]["e_local"], 1),
+                     "bf16_ms": wl[a]["ms_per_step"], "w4a16_ms": wl[b]["ms_per_step"],
+                     "bf16_over_w4a16": round(wl[a]["ms_per_step"] / wl[b]["ms_per_step"], 3)}
+        for a, b in (("decode", "w4a16_decode"), ("prefill", "w4a16"), ("skewed_shared", "w4a16_skewed"))
+        if a in wl and b in wl}
     print(json.dumps(out), flush=True)
 
 

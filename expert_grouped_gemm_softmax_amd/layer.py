@@ -54,6 +54,21 @@ class ExpertWeights:
         return self.h_fp8 if self.fp8 else self.w_down.dtype
 
 
+# Measured on one MI355X (bench.py, paired workloads with the same routing): W4A16 over bf16
+# expert weights, step time ratio bf16 / W4A16 -- 1.53 at 10 rows per expert (decode), 1.01 at
+# 160 (prefill), 0.81 under the skewed routing (1280 rows per expert, hot experts of 8192): int4
+# pays where the expert weights are streamed (fewer bytes), bf16 where the matrix units bind (its
+# prefill tiles copy operands straight to LDS, int4 dequantises through registers).
+W4A16_MAX_ROWS_PER_EXPERT = 192
+
+
+def choose_weight_format(rows_per_expert: float) -> str:
+    """Weight format for the routed experts by the expected rows per expert (T * k / E): "int4"
+    (W4A16) up to W4A16_MAX_ROWS_PER_EXPERT rows, where this library measured it at least as fast
+    as bf16, else "bf16".  The layer's accuracy is the same either way (both meet the parity bar)."""
+    return "int4" if rows_per_expert <= W4A16_MAX_ROWS_PER_EXPERT else "bf16"
+
+
 def _t(a: np.ndarray, device) -> torch.Tensor:
     """numpy -> device tensor; uint16 arrays are bf16 bit patterns, uint8 arrays fp8 bytes."""
     if a.dtype == np.uint16:

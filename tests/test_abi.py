@@ -254,3 +254,14 @@ def test_router_entry_points_validation(L):
     assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 0, F, F, F, F, None) == INV
     assert L.moe_route_hidden(F, 1, F, None, 8, 64, 16, 17, F, F, F, F, None) == INV
     assert L.moe_route_hidden(F, 0, F, None, 8, 64, 1025, 2, F, F, F, F, None) == INV
+
+
+def test_weight_format_rule():
+    """The bf16 / W4A16 choice by rows per expert (host logic): int4 where the expert weights are
+    streamed (decode), bf16 where the matrix units bind (skewed hot experts)."""
+    from expert_grouped_gemm_softmax_amd.layer import W4A16_MAX_ROWS_PER_EXPERT, choose_weight_format
+    assert choose_weight_format(10) == "int4"          # decode: 512 tokens x 10 / 512 experts
+    assert choose_weight_format(160) == "int4"         # prefill
+    assert choose_weight_format(1280) == "bf16"        # skewed routing, T = 8192
+    assert choose_weight_format(W4A16_MAX_ROWS_PER_EXPERT) == "int4"
+    assert choose_weight_format(W4A16_MAX_ROWS_PER_EXPERT + 1) == "bf16"
