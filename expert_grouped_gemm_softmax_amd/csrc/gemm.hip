@@ -239,7 +239,7 @@ struct AChunk {
 };
 template <class C>
 struct WChunk {
-  u32x4 b[C::B_UNITS][C::Q4 ? 1 : (C::W8 ? 2 : C::R)];   // int4: 4 words; fp8: 32 bytes; dense: R pieces
+  u32x4 b[C::B_UNITS][C::Q4 ? 1 : (C::W8 ? 2 : C::R)];   // int4: 4 words; fp8: two 16-byte pieces; dense: R pieces
   u32x2 s[C::B_UNITS];
 };
 template <class C>
@@ -267,7 +267,9 @@ struct TileCtx {
   int kn_m[C::KN ? C::B_PIECES : 1];                // [K][N]: matrix of each piece (wave-uniform)
   uint32_t kn_soff;                                 // [K][N]: byte offset of the tile's first column
   int b_dst[C::B_UNITS][(C::Q4 || C::W8) ? 4 : 1];  // int4: LDS destination of each dequantised column;
-                                                    // fp8: of each 16-byte chunk of the unit
+                                                    // fp8: of each 16-byte LDS chunk (two per piece)
+  uint32_t w8_off[C::W8 ? 2 * C::B_UNITS : 1];      // fp8: byte offset of each piece in chunk 0
+  int w8_m[C::W8 ? 2 * C::B_UNITS : 1];             // fp8: matrix of each piece (wave-uniform)
   bool b_swap[C::B_UNITS];                          // int4: columns written in swapped pairs
   const u16* es[C::NW];                             // fp8: scales of the tile's first column, per matrix
   int nK, row_bytes, s_row_bytes, group_size;
@@ -300,10 +302,14 @@ __device__ __forceinline__ void load_w(const TileCtx<C>& t, int kc, WChunk<C>& c
 #pragma unroll
   for (int i = 0; i < C::B_UNITS; ++i) {
     if constexpr (C::W8) {
-      // 32 consecutive k of one column: K bytes per column, the chunk at byte kc * 64
-      const uint32_t o = t.b_off[i] + (uint32_t)kc * C::KC;
-      ch.b[i][0] = __builtin_amdgcn_raw_buffer_load_b128(t.wr[i], o, 0, 2);
-      ch.b[i][1] = __builtin_amdgcn_raw_buffer_load_b128(t.wr[i], o + 16, 0, 2);
+      // two pieces of 16 consecutive k of one column each: K bytes per column, the chunk at byte
+      // kc * 64
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        __amdgpu_buffer_rsrc_t w = t.wr[0];
+        if constexpr (C::NW == 2) w = t.w8_m[2 * i + h] ? t.wr[1] : t.wr[0];
+        ch.b[i][h] = __builtin_amdgcn_raw_buffer_load_b128(w, t.w8_off[2 * i + h] + (uint32_t)kc * C::KC, 0, 2);
+      }
     } else if constexpr (!C::Q4) {
       // piece x = i*R + r covers weight rows SLICE_ROWS*x .. SLICE_ROWS*(x+1)-1 of the NW*BN tile rows
 #pragma unroll
@@ -547,19 +553,26 @@ __device__ __forceinline__ void tile_body(const TileCtx<C>& t, u16* buf0, u16* b
     }
     if (kc < nK) compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
   } else if constexpr (C::REGSETS == 4) {
-    // One LDS buffer, four chunks in registers (the caller keeps K a multiple of 4 chunks): the
-    // quantised weights carry half or a quarter of the bytes of a 16-bit chunk, so a
-    // decode-shaped tile keeps twice as many chunks in flight to hold the same bytes in flight.
-    Chunk<C> c[4];
+    // One LDS buffer, RS = 4 chunks in registers (the caller keeps K a multiple of RS chunks):
+    // the quantised weights carry half or a quarter of the bytes of a 16-bit chunk, so a
+    // decode-shaped tile keeps more chunks in flight to hold more bytes in flight.  The prologue
+    // issues the chunks in the loop's order: the wait at the loop head covers the oldest chunk on
+    // both entry edges only when they leave the loads in the same order (else the head waits for
+    // every load in flight, once per RS chunks).
+    constexpr int RS = C::REGSETS;
+    Chunk<C> c[RS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) load_chunk(t, r, c[r]);
-    for (; kc < nK; kc += 4) {
+    for (int r = 0; r < RS; ++r) {
+      load_chunk(t, r, c[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; kc < nK; kc += RS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < RS; ++r) {
         store_chunk(t, c[r], buf0);
         __syncthreads();
         compute_chunk<C, NM>(buf0, acc, arow, bcol, kofs);
-        load_chunk(t, kc + 4 + r, c[r]);                 // clamped past the end
+        load_chunk(t, kc + RS + r, c[r]);                // clamped past the end
         __syncthreads();
       }
     }
@@ -698,19 +711,26 @@ void k_gemm_bf16(GemmParams p) {
       t.kn_soff = (uint32_t)n0 * 2;
       t.row_bytes = p.N * 2;
     } else if constexpr (C::W8) {
-      // fp8 [e][n][k]: unit u of a matrix covers k = 32 (u % 2) .. + 31 of column u / 2, so two
-      // lanes read one column's 64 bytes of a chunk; each 16-lane LDS pass writes 8 columns (4
-      // even, 4 odd rows) at two chunk positions each, one per bank group.
-      constexpr int per_m = KC * BN / 32;
-      static_assert(per_m % 64 == 0, "a wave's units read one matrix");
+      // fp8 [e][n][k]: piece x of a thread is piece P = tid + NT x of the chunk, 16 consecutive
+      // k (bytes 16 (P % 4) .. + 15) of column (P / 4) % BN of matrix P / (4 BN): four lanes
+      // read one column's 64 bytes, so each load of a wave covers 16 whole 64-byte column
+      // segments.  A piece fills LDS chunks 2 (P % 4) and + 1 of its column; each 16-lane pass
+      // writes 4 columns (2 even, 2 odd rows) at chunks 0, 2, 4, 6 (or 1, 3, 5, 7), which the
+      // row swizzle spreads over all 16-byte bank slots.
+      constexpr int per_m = KC * BN / 16;
+      static_assert(per_m % 64 == 0, "a wave's pieces read one matrix");
 #pragma unroll
-      for (int i = 0; i < C::B_UNITS; ++i) {
-        const int m = __builtin_amdgcn_readfirstlane((tid + NT * i) / per_m);
-        t.wr[i] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)e * w_bytes, w_bytes);
-        const int u = (tid + NT * i) % per_m, n = u / 2, kq = u % 2;
-        t.b_off[i] = (uint32_t)((n0 + n) * p.K + kq * 32);
+      for (int m = 0; m < C::NW; ++m)
+        t.wr[m] = make_rsrc(static_cast<const char*>(m == 0 ? p.w0 : p.w1) + (size_t)e * w_bytes, w_bytes);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) t.b_dst[i][c] = lds_off_rows(m * BN + n, kq * 4 + c);
+      for (int x = 0; x < 2 * C::B_UNITS; ++x) {
+        const int P = tid + NT * x;
+        const int m = __builtin_amdgcn_readfirstlane(P / per_m);
+        const int n = (P / 4) % BN, kq = P % 4;
+        t.w8_m[x] = m;
+        t.w8_off[x] = (uint32_t)((n0 + n) * p.K + kq * 16);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) t.b_dst[x / 2][2 * (x % 2) + c] = lds_off_rows(m * BN + n, 2 * kq + c);
       }
 #pragma unroll
       for (int m = 0; m < C::NW; ++m)
