@@ -285,7 +285,7 @@ def copy_calibration():
 # ---------------------------------------------------------------------------------------------
 # One workload
 # ---------------------------------------------------------------------------------------------
-def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -> dict:
+def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None, min_warmup_s: float = MIN_WARMUP_S) -> dict:
     """Time `steps` whole steps of one workload (after `warmup`), then per-step latencies and a
     per-kernel breakdown in separate event-bracketed passes; rooflines; the CPU oracle."""
     import numpy as np
@@ -305,7 +305,7 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
         layer.forward(x, logits)
     torch.cuda.synchronize()
     warm_run, t_warm = warmup, time.perf_counter()
-    while time.perf_counter() - t_warm < MIN_WARMUP_S:
+    while time.perf_counter() - t_warm < min_warmup_s:
         for _ in range(5):
             layer.forward(x, logits)
         torch.cuda.synchronize()
@@ -365,6 +365,19 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
     kus = {n: float(np.mean([bev[i][j].elapsed_time(bev[i][j + 1]) * 1e3 for i in range(nb)]))
            for j, n in enumerate(names)}
 
+    # The two GEMMs launched back to back, 10 launches between two events: per-launch kernel time
+    # without an event's dispatch wait in front of each launch (which inflates a bracketed
+    # 100-us kernel by several percent; the kernel traces agree with these figures).
+    b2b = {}
+    for n, fn in (("gate_up", lambda: layer.step_gate_up(x, b)), ("down", lambda: layer.step_down(x, b))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b2b[n] = e0.elapsed_time(e1) * 1e3 / 10
+
     # The router projection x W_r (+ bias) and routing from the hidden states (moe_route_hidden),
     # timed apart from the step: the workloads' own steps start from the router logits.
     from expert_grouped_gemm_softmax_amd import ops
@@ -403,10 +416,14 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
 
     wk = work(cfg, n_loc, nonempty)
     roof = roofline(cfg, wk["gate_up"]["flops"], wk["gate_up"]["bytes"], gu_us * 1e-6, att)
+    b2b_roof = roofline(cfg, wk["gate_up"]["flops"], wk["gate_up"]["bytes"], b2b["gate_up"] * 1e-6, att)
     roof.update({"kernel": "routed grouped GEMM gate/up + SwiGLU", "time_us": round(gu_us, 1),
                  "algorithmic_bytes": int(wk["gate_up"]["bytes"]), "algorithmic_flops": int(wk["gate_up"]["flops"]),
-                 "traffic": measured_traffic(name, "gate_up"), "samples": len(sampled)})
-    kernels = {"down": roofline(cfg, wk["down"]["flops"], wk["down"]["bytes"], kus["down"] * 1e-6, att)}
+                 "traffic": measured_traffic(name, "gate_up"), "samples": len(sampled),
+                 "back_to_back": {"time_us": round(b2b["gate_up"], 1), "achieved": b2b_roof["achieved"],
+                                  "frac": b2b_roof["frac"]}})
+    kernels = {"down": roofline(cfg, wk["down"]["flops"], wk["down"]["bytes"], b2b["down"] * 1e-6, att)}
+    kernels["down"]["time_us"] = round(b2b["down"], 1)
     if cfg.shared_I:
         kernels["shared"] = roofline(cfg, wk["shared"]["flops"], wk["shared"]["bytes"], kus["shared"] * 1e-6, att)
     pair_s = n_loc / (ms_per_step / 1e3)
@@ -445,7 +462,8 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None) -
 def run_child(name: str, args) -> dict:
     """One sub-workload in a child process of its own (this process has not touched the GPU)."""
     cmd = [sys.executable, "-u", os.path.abspath(__file__), "--child", "--workload", name,
-           "--steps", str(args.steps), "--warmup", str(args.warmup), "--cpu-seconds", str(args.cpu_seconds)]
+           "--steps", str(args.steps), "--warmup", str(args.warmup), "--cpu-seconds", str(args.cpu_seconds),
+           "--min-warmup-s", str(args.min_warmup_s)]
     if args.no_cpu_baseline:
         cmd.append("--no-cpu-baseline")
     print(f"[bench] child: {name}", file=sys.stderr, flush=True)
@@ -465,6 +483,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S,
+                    help="warm-up continues past --warmup steps until this many seconds have passed "
+                         "(0 for counter runs, which need few dispatches)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "
@@ -475,7 +496,7 @@ def main():
         return
     cpu_s = None if args.no_cpu_baseline else args.cpu_seconds
     if args.child:
-        print(json.dumps(measure(args.workload, args.steps, args.warmup, cpu_s)), flush=True)
+        print(json.dumps(measure(args.workload, args.steps, args.warmup, cpu_s, min_warmup_s=args.min_warmup_s)), flush=True)
         return
 
     print(f"[bench] pid {os.getpid()}", file=sys.stderr, flush=True)
@@ -483,7 +504,8 @@ def main():
     subs = {} if args.workload else {n: run_child(n, args) for n in SUBS}   # before this process uses the GPU
 
     att = attainable_peaks()
-    h = measure(head, args.steps, args.warmup, None if cpu_s is None else max(cpu_s, 12.0), att)
+    h = measure(head, args.steps, args.warmup, None if cpu_s is None else max(cpu_s, 12.0), att,
+                min_warmup_s=args.min_warmup_s)
     for r in subs.values():                       # measured ceilings of this machine for the children too
         if att:
             for rr in [r["roofline"]] + list(r["kernel_rooflines"].values()):
