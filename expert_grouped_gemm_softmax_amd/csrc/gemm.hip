@@ -446,10 +446,11 @@ __device__ __forceinline__ void load_pair(const TileCtx<C>& t, int kc, Chunk<C>&
   for (int i = 0; i < C::B_UNITS; ++i)
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
+      constexpr int PC = C::NT / 8;                 // columns per piece load of the workgroup
       const int q = 4 * i + x;
-      __amdgpu_buffer_rsrc_t w = t.wr[0];
-      if constexpr (C::NW == 2) w = t.w8_m[q] ? t.wr[1] : t.wr[0];
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(w, t.w8_off[q] + (uint32_t)kc * C::KC, 0, 2);
+      const int mq = (PC * q) / C::BN, cq = (PC * q) % C::BN;   // matrix and first column of piece q
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(t.wr[mq], t.w8_off[0] + (uint32_t)(cq * t.row_bytes) +
+                                                            (uint32_t)kc * C::KC, 0, 2);
       if (x < 2) e.w.b[i][x] = v;
       else o.w.b[i][x - 2] = v;
     }
@@ -467,12 +468,15 @@ __device__ __forceinline__ void store_pair_chunk(const TileCtx<C>& t, const Chun
   for (int i = 0; i < C::B_UNITS; ++i)
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
+      constexpr int PC = C::NT / 8;
+      const int q = 4 * i + x;
+      const int row = (PC * q) / C::BN * C::BN + (PC * q) % C::BN;   // first tile row of piece q
       const u32x4 v = x < 2 ? e.w.b[i][x] : o.w.b[i][x - 2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {                  // eight k per 16-byte LDS chunk
         const u32x2 lo = fp8x4_to_16<C::F16>(v[2 * c]);
         const u32x2 hi = fp8x4_to_16<C::F16>(v[2 * c + 1]);
-        *reinterpret_cast<u32x4*>(sB + t.b_dst[i][2 * x + c]) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        *reinterpret_cast<u32x4*>(sB + t.b_dst[0][c] + row * 64) = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     }
 }
@@ -789,19 +793,15 @@ void k_gemm_bf16(GemmParams p) {
         // belongs to the pair's first or second chunk by (Q % 8) / 4 and fills LDS chunks 2 kq
         // and + 1 (kq = Q % 4) of its column: the 4 lanes of a group that store one chunk write
         // 4 slots of one row.
-        constexpr int per_m = 2 * KC * BN / 16;
-        static_assert(per_m % 64 == 0, "a wave's pieces read one matrix");
+        // Piece q's columns are NT / 8 q .. + NT / 8 - 1 of the tile, a compile-time matrix and
+        // first column (NT / 8 divides BN, a multiple of 16 rows: the same swizzle), so a lane
+        // keeps one global offset and one LDS destination per chunk half.
+        static_assert(NT / 8 <= BN && BN % (NT / 8) == 0 && (NT / 8) % 16 == 0, "piece columns");
         t.w8_hi = ((lane & 7) >> 2) != 0;
+        t.row_bytes = p.K;
+        t.w8_off[0] = (uint32_t)((n0 + tid / 8) * p.K + (lane & 7) * 16);
 #pragma unroll
-        for (int x = 0; x < 4 * C::B_UNITS; ++x) {
-          const int Q = tid + NT * x;
-          const int m = __builtin_amdgcn_readfirstlane(Q / per_m);
-          const int n = (Q / 8) % BN, kq = Q % 4;
-          t.w8_m[x] = m;
-          t.w8_off[x] = (uint32_t)((n0 + n) * p.K + (Q % 8) * 16);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) t.b_dst[x / 4][2 * (x % 4) + c] = lds_off_rows(m * BN + n, 2 * kq + c);
-        }
+        for (int c = 0; c < 2; ++c) t.b_dst[0][c] = lds_off_rows(tid / 8, 2 * (lane & 3) + c);
       } else {
         // Piece x of a thread is piece P = tid + NT x of the chunk, 16 consecutive k (bytes
         // 16 (P % 4) .. + 15) of column (P / 4) % BN of matrix P / (4 BN): four lanes read one
@@ -1059,6 +1059,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory instructions of this wave are outstanding (they complete in
+// issue order, so every older one has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 template <class C>
 struct DmaCtx {
@@ -1085,7 +1089,21 @@ __device__ __forceinline__ void dma_chunk(const DmaCtx<C>& t, int kc, int stage)
   }
 }
 
-template <class C, typename OutT, int NM>
+template <class C>
+__device__ __forceinline__ void dma_a(const DmaCtx<C>& t, int kc, int stage) {
+  const uint32_t st = t.lds + (uint32_t)stage * C::STAGE * 2;
+#pragma unroll
+  for (int j = 0; j < C::A_INST; ++j)
+    lds_dma16(t.ar, t.a_voff[j], (uint32_t)kc * 128, st + 8 * (t.wave + C::NWAVES * j) * 128);
+}
+
+// BREG: the tile's weight chunks go through registers two chunks ahead (global loads, then
+// ds_write to where the copies would land), its activation chunks are copied one chunk ahead.
+// For gate/up tiles whose expert has a single m-tile, whose weights therefore stream from HBM
+// once: the register path gives their misses two chunks of time (prefill gate/up -4 %); tiles of
+// experts with several m-tiles, whose weights the m-tiles share in L2, keep the copies (there the
+// register path measured 6 % slower).
+template <class C, typename OutT, int NM, bool BREG>
 __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O, int N, int lane, int wrow0, int wcol0,
                                          const TileCoord& tc) {
   f32x4 acc[C::NW][NM > 0 ? NM : 1][C::NTL];
@@ -1097,21 +1115,73 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
       for (int j = 0; j < C::NTL; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int arow = wrow0 + (lane & 15), bcol = wcol0 + (lane & 15), kofs = (lane >> 4) * 8;
   const int nK = t.nK;
+  // weights through registers: chunk kc + 1's weights are stored to LDS and chunk kc + 2's loaded
+  // at the top of step kc; the loads land where the copies would (same lanes, same offsets)
+  u32x4 wb[BREG ? C::B_INST : 1];
+  auto wload = [&](int kc) {
+    if constexpr (BREG) {
+      kc = min(kc, nK - 1);
+#pragma unroll
+      for (int j = 0; j < C::B_INST; ++j) {
+        __amdgpu_buffer_rsrc_t w = t.wr[0];
+        if constexpr (C::NW == 2) w = t.b_m[j] ? t.wr[1] : t.wr[0];
+        wb[j] = __builtin_amdgcn_raw_buffer_load_b128(w, t.b_voff, t.b_soff[j] + (uint32_t)kc * 128, 0);
+      }
+    }
+  };
+  auto wstore = [&](int stage) {
+    if constexpr (BREG) {
+      u16* sB = smem + stage * C::STAGE + C::A_ELEMS;
+#pragma unroll
+      for (int j = 0; j < C::B_INST; ++j)
+        *reinterpret_cast<u32x4*>(sB + 8 * (t.wave + C::NWAVES * j) * 64 + lane * 8) = wb[j];
+    }
+  };
   wait_vmcnt0();
-  dma_chunk(t, 0, 0);
+  if constexpr (BREG) {
+    wload(0);
+    wstore(0);
+    dma_a(t, 0, 0);
+    wload(1);
+  } else {
+    dma_chunk(t, 0, 0);
+  }
   for (int kc = 0; kc < nK; ++kc) {
-    wait_vmcnt0();                                 // this wave's loads of chunk kc
+    if constexpr (BREG) wait_vmcnt_n<C::B_INST>();   // this wave's copies of chunk kc (weights of kc + 1 fly)
+    else wait_vmcnt0();                                 // this wave's loads of chunk kc
     __syncthreads();                               // everyone's; and the other buffer is free
-    if (kc + 1 < nK) dma_chunk(t, kc + 1, (kc + 1) & 1);
+    if constexpr (BREG) {
+      if (kc + 1 < nK) {
+        wstore((kc + 1) & 1);
+        dma_a(t, kc + 1, (kc + 1) & 1);
+      }
+      wload(kc + 2);                               // clamped past the end
+    } else {
+      if (kc + 1 < nK) dma_chunk(t, kc + 1, (kc + 1) & 1);
+    }
     if constexpr (NM > 0) {
       const u16* sA = smem + (kc & 1) * C::STAGE;
       const u16* sB = sA + C::A_ELEMS;
       // Every operand of the chunk is read before its MFMAs: LDS reads return in order, so each
-      // MFMA waits only for its own operands and the later reads overlap the earlier MFMAs.
+      // MFMA waits only for its own operands and the later reads overlap the earlier MFMAs.  With
+      // weights in registers (16 more) one 32-k step's operands are read at a time.
       constexpr int KS = C::KC / 32;
       u32x4 av[KS][NM], bv[KS][C::NW][C::NTL];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (BREG) {
+          if (ks > 0) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < C::NW; ++m)
+#pragma unroll
+              for (int j = 0; j < C::NTL; ++j)
+#pragma unroll
+                for (int i = 0; i < NM; ++i)
+                  acc[m][i][j] = mma<C::F16>(av[ks - 1][i], bv[ks - 1][m][j], acc[m][i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < NM; ++i)
           av[ks][i] = *reinterpret_cast<const u32x4*>(sA + lds_off_rows(arow, (ks * 32 + kofs) >> 3) + i * 16 * C::WM * 64);
@@ -1123,7 +1193,7 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
       }
       __builtin_amdgcn_sched_barrier(0);           // keep the reads ahead of the MFMAs
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = BREG ? KS - 1 : 0; ks < KS; ++ks)
 #pragma unroll
         for (int m = 0; m < C::NW; ++m)
 #pragma unroll
@@ -1151,12 +1221,12 @@ __device__ __forceinline__ void dma_tile(const DmaCtx<C>& t, u16* smem, OutT* O,
       }
 }
 
-template <class C, typename OutT, int NM>
+template <class C, typename OutT, int NM, bool BREG>
 __device__ __forceinline__ void dma_dispatch(int nm, const DmaCtx<C>& t, u16* smem, OutT* O, int N, int lane, int wrow0,
                                              int wcol0, const TileCoord& tc) {
   if constexpr (NM <= C::MT) {
-    if (nm == NM) dma_tile<C, OutT, NM>(t, smem, O, N, lane, wrow0, wcol0, tc);
-    else dma_dispatch<C, OutT, NM + 1>(nm, t, smem, O, N, lane, wrow0, wcol0, tc);
+    if (nm == NM) dma_tile<C, OutT, NM, BREG>(t, smem, O, N, lane, wrow0, wcol0, tc);
+    else dma_dispatch<C, OutT, NM + 1, BREG>(nm, t, smem, O, N, lane, wrow0, wcol0, tc);
   }
 }
 
@@ -1210,7 +1280,15 @@ void k_gemm_dma(GemmParams p) {
       t.b_m[j] = rb / BN;
       t.b_soff[j] = (uint32_t)(tc.n0 + rb % BN) * row_bytes;
     }
-    dma_dispatch<C, OutT, 0>(nm, t, smem_dma, O, p.N, lane, wrow0, wcol0, tc);
+    // gate/up tiles of an expert with one m-tile: its weights stream once, through registers
+    const bool once = C::GU && __builtin_amdgcn_readfirstlane(s_goff[tc.e + 1] - s_goff[tc.e]) <= BM;
+    if constexpr (C::GU) {
+      if (once) {
+        dma_dispatch<C, OutT, 0, true>(nm, t, smem_dma, O, p.N, lane, wrow0, wcol0, tc);
+        continue;
+      }
+    }
+    dma_dispatch<C, OutT, 0, false>(nm, t, smem_dma, O, p.N, lane, wrow0, wcol0, tc);
   }
 }
 
@@ -1269,10 +1347,6 @@ __device__ __forceinline__ TileCoord reg_tile_coord(const RegTable& r, int n_gro
   return {e, row0, min(BM, g1 - row0), nt * BN};
 }
 
-// Wait until at most N vector memory instructions of this wave are outstanding (they complete in
-// issue order, so every older one has landed).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_n() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 // LDS: activation buffers [2][A_ELEMS], then weight buffers [3][B_ELEMS].
 template <class C>
@@ -1732,8 +1806,8 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
     // dense: two workgroups per CU (half as many weight streams, each workgroup streams several
     // tiles back to back): 2 % faster than four on the decode-shaped down projection
     if (q4) {
-      if (k4) return f32out ? run_cfg_dn<32, 128, 1, 4, 1, 4, 4, true, true, float>(p, s)
-                            : run_cfg_dn<32, 128, 1, 4, 1, 4, 4, true, true, _Float16>(p, s);
+      // four register sets with fp16 output; the fp32 epilogue's registers leave room for two
+      if (k4 && !f32out) return run_cfg_dn<32, 128, 1, 4, 1, 4, 4, true, true, _Float16>(p, s);
       return run_dn<32, 128, 1, 4, 1, 4, 2>(p, q4, f16, f32out, s);
     }
     return run_dn<32, 128, 1, 4, 1, 2, 2>(p, q4, f16, f32out, s);
