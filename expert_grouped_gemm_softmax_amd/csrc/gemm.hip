@@ -344,37 +344,53 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& v) {
   return r;
 }
 
+// int4 tiles hold the eight k of each 16-byte LDS chunk, activations and weights alike, in the
+// order k0 k4 k1 k5 k2 k6 k3 k7: the order in which the int4 dequantisation below produces them
+// with the fewest instructions.  An MFMA multiplies the operand elements of equal position, so
+// equal permutations of both operands leave every product, and the sum over the chunk, the same.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_il(const u32x4& v) {
+  return u32x4{pack_f16x2(__uint_as_float(v[0] << 16), __uint_as_float(v[2] << 16)),
+               pack_f16x2(__uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[2] & 0xffff0000u)),
+               pack_f16x2(__uint_as_float(v[1] << 16), __uint_as_float(v[3] << 16)),
+               pack_f16x2(__uint_as_float(v[1] & 0xffff0000u), __uint_as_float(v[3] & 0xffff0000u))};
+}
+__device__ __forceinline__ u32x4 f16x8_il(const u32x4& v) {
+  // v_perm_b32 byte selectors: 0-3 pick bytes of the second operand, 4-7 of the first
+  return u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+               __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+}
+
 template <class C>
 __device__ __forceinline__ void store_a(const TileCtx<C>& t, const AChunk<C>& ch, u16* buf) {
   u16* sA = buf;
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
     u32x4 v = ch.a[i];
-    if constexpr (C::ACVT) v = bf16x8_to_f16x8(v);
+    if constexpr (C::Q4) v = C::ACVT ? bf16x8_to_f16x8_il(v) : f16x8_il(v);
+    else if constexpr (C::ACVT) v = bf16x8_to_f16x8(v);
     *reinterpret_cast<u32x4*>(sA + t.a_lds + C::SLICE_ROWS * i * 64) = v;
   }
 }
 
 // Eight int4 weights (the nibbles of one word, k ascending) times their scale, exactly, as eight
-// fp16 values: nibble u (two's complement q) -> u ^ 8 = q + 8, which placed in the low mantissa
-// bits of fp16 1024 gives 1032 + q; subtracting 1032 leaves q exactly, and q * (s * 2^8) has at
-// most 3 + 8 significant bits, so the packed fp16 product is exact.  Dword i holds the weights of
-// k = 2i (low half) and 2i + 1.
+// fp16 values in the int4 tiles' order k0 k4 | k1 k5 | k2 k6 | k3 k7.  Nibble u (two's complement
+// q) -> u ^ 8 = q + 8.  Masking the word with 0x000f000f (nibbles 0 and 4) and setting the
+// exponent bits of 1024 in both halves gives the fp16 pair 1032 + q; with 0x00f000f0 (nibbles 1
+// and 5) the nibble sits four bits higher, 1024 + 16 (q + 8), and times 1/16 minus 72 leaves q.
+// The word shifted down by 8 bits gives nibbles 2, 6 and 3, 7 the same way.  Each step is exact
+// in fp16 (all values are integers below 2048), and q * (s * 2^8) has at most 3 + 8 significant
+// bits, so the packed fp16 product is exact.
 __device__ __forceinline__ u32x4 dequant_int4_f16(uint32_t word, f16x2 scale2) {
-  const uint32_t w = word ^ 0x88888888u;
-  const uint32_t lo = w & 0x0f0f0f0fu;             // nibbles 0, 2, 4, 6 in bytes 0..3
-  const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;      // nibbles 1, 3, 5, 7
-  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // bytes: lo byte i, 0, hi byte i, 0 (v_perm_b32 selector 0x0c yields a zero byte)
-    const uint32_t sel = 0x0c000c00u | (uint32_t)i | ((uint32_t)(4 + i) << 16);
-    const uint32_t t = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-    const f16x2 q = __builtin_bit_cast(f16x2, t) - bias;
-    r[i] = __builtin_bit_cast(uint32_t, q * scale2);
-  }
-  return r;
+  const uint32_t x = word ^ 0x88888888u, y = x >> 8;
+  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const f16x2 q0 = __builtin_bit_cast(f16x2, (x & 0x000f000fu) | 0x64006400u) + bias;
+  const f16x2 q1 = __builtin_bit_cast(f16x2, (x & 0x00f000f0u) | 0x64006400u) * inv16 + bias16;
+  const f16x2 q2 = __builtin_bit_cast(f16x2, (y & 0x000f000fu) | 0x64006400u) + bias;
+  const f16x2 q3 = __builtin_bit_cast(f16x2, (y & 0x00f000f0u) | 0x64006400u) * inv16 + bias16;
+  return u32x4{__builtin_bit_cast(uint32_t, q0 * scale2), __builtin_bit_cast(uint32_t, q1 * scale2),
+               __builtin_bit_cast(uint32_t, q2 * scale2), __builtin_bit_cast(uint32_t, q3 * scale2)};
 }
 
 // bf16 scale bits -> fp16 pair of the scale times 2^8 (exact for 2^-22 <= s < 32)
@@ -1806,9 +1822,11 @@ hipError_t launch_grouped_gemm(const moe_gemm_args& a, hipStream_t s) {
     // dense: two workgroups per CU (half as many weight streams, each workgroup streams several
     // tiles back to back): 2 % faster than four on the decode-shaped down projection
     if (q4) {
-      // four register sets with fp16 output; the fp32 epilogue's registers leave room for two
+      // four register sets with fp16 output; otherwise two, at three workgroups per CU (the fp32
+      // epilogue and the activation reordering of int4 tiles need more than a quarter of the
+      // registers)
       if (k4 && !f32out) return run_cfg_dn<32, 128, 1, 4, 1, 4, 4, true, true, _Float16>(p, s);
-      return run_dn<32, 128, 1, 4, 1, 4, 2>(p, q4, f16, f32out, s);
+      return run_dn<32, 128, 1, 4, 1, 3, 2>(p, q4, f16, f32out, s);
     }
     return run_dn<32, 128, 1, 4, 1, 2, 2>(p, q4, f16, f32out, s);
   }
