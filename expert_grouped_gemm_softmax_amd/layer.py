@@ -55,7 +55,7 @@ class ExpertWeights:
 
 
 # Measured on one MI355X (bench.py, paired workloads with the same routing): W4A16 over bf16
-# expert weights, step time ratio bf16 / W4A16 -- 1.72 at 10 rows per expert (decode), 1.07 at
+# expert weights, step time ratio bf16 / W4A16 -- 1.7-1.8 at 10 rows per expert (decode), 1.07 at
 # 160 (prefill), 0.81 under the skewed routing (1280 rows per expert, hot experts of 8192): int4
 # pays where the expert weights are streamed (fewer bytes), bf16 where the matrix units bind (its
 # prefill tiles copy operands straight to LDS, int4 dequantises through registers).
