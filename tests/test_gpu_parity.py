@@ -398,6 +398,41 @@ def test_stated_layout_full_decode_every_token():
                  "decode stated layout all 512 tokens")
 
 
+# More than 16,384 pairs: the multi-kernel permutation with its caller workspace.
+GRAPH_LARGE_PERMUTE = W.MoEConfig("mid", T=2100, H=256, E=64, k=8, I=128, e_first=0, e_local=32)
+
+
+@pytest.mark.parametrize("variant", ["small_m", "large_m"])
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_shared", "int4_g128", "fp8", "large_permute"])
+def test_layer_step_replays_from_a_captured_graph(name, variant):
+    """The library launches kernels only (no allocation, memset or synchronisation), so a whole
+    layer step captured in a graph replays bit for bit like the eager step.  Each replay follows
+    eager work that clears the step's buffers and runs another layer, and is checked."""
+    cfg = GRAPH_LARGE_PERMUTE if name == "large_permute" else MID[name]
+    print(f"graph capture: {name} {variant} T={cfg.T} pairs={cfg.T * cfg.k}", flush=True)
+    inp = W.make_inputs(cfg)
+    x, logits, wts = upload(inp, cfg, _dev())
+    layer = MoELayer.from_config(cfg, wts)
+    other = MoELayer.from_config(cfg, wts)
+    if variant == "small_m":
+        layer.m_hint = lambda T: 8
+    y_eager = layer.forward(x, logits).clone()      # the eager step also allocates the buffers
+    torch.cuda.synchronize()
+    b = layer.buffers(cfg.T, x.device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_graph = layer.forward(x, logits)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for buf in (b.y, b.o, b.h, b.sorted_pairs, b.pair_pos, b.group_offsets, b.blob):
+            buf.zero_()
+        other.forward(x * (rep + 2), logits)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph.view(torch.int32), y_eager.view(torch.int32)), f"replay {rep}"
+
+
 def test_layer_single_token_and_single_expert():
     cfg = W.MoEConfig("one", T=1, H=128, E=4, k=2, I=64, e_first=1, e_local=1)
     inp = W.make_inputs(cfg)
