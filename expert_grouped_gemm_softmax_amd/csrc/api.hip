@@ -29,6 +29,11 @@ namespace {
 
 inline bool fits_i32(long long v) { return v >= 0 && v < (long long)INT_MAX; }
 
+// Alignment of device pointers (NULL passes; required arguments are checked separately): index,
+// routing and fp32 vector arrays to 4 bytes, matrices that kernels move 16 bytes at a time to 16.
+inline bool al4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+inline bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 // Status of one enqueue: the runtime's last-error slot is cleared first, so an error left there by
 // an earlier, unrelated call of the caller is not reported as this call's failure.
 template <class F>
@@ -58,6 +63,7 @@ MOE_API const char* moe_status_string(int status) {
 MOE_API moe_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
                              void* stream) {
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!al4(logits) || !al4(topk_ids) || !al4(topk_w)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * E)) return MOE_ERR_INVALID_ARG;
   return enqueue([&] { return moe::launch_route(logits, T, E, k, topk_ids, topk_w, nullptr, as_stream(stream)); });
@@ -66,6 +72,7 @@ MOE_API moe_status moe_route(const float* logits, int T, int E, int k, int32_t* 
 MOE_API moe_status moe_route_packed(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
                                     int32_t* blob, void* stream) {
   if (!logits || !blob || (topk_ids == nullptr) != (topk_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!al4(logits) || !al4(blob) || !al4(topk_ids) || !al4(topk_w)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
   if (!fits_i32((long long)T * E) || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
   return enqueue([&] { return moe::launch_route(logits, T, E, k, topk_ids, topk_w, blob, as_stream(stream)); });
@@ -74,12 +81,14 @@ MOE_API moe_status moe_route_packed(const float* logits, int T, int E, int k, in
 MOE_API moe_status moe_pack_routing(const int32_t* topk_ids, const float* topk_w, int T, int k,
                                     int32_t* blob, void* stream) {
   if (!topk_ids || !topk_w || !blob) return MOE_ERR_INVALID_ARG;
+  if (!al4(topk_ids) || !al4(topk_w) || !al4(blob)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
   return enqueue([&] { return moe::launch_pack(topk_ids, topk_w, T, k, blob, as_stream(stream)); });
 }
 
 MOE_API moe_status moe_prepare_router_weights(const float* wr, int H, int E, void* out, void* stream) {
   if (!wr || !out) return MOE_ERR_INVALID_ARG;
+  if (!al4(wr) || !al16(out)) return MOE_ERR_INVALID_ARG;
   if (H < 1 || E < 1 || E > 1024 || H > (1 << 22) || !fits_i32((long long)H * E)) return MOE_ERR_INVALID_ARG;
   return enqueue([&] { return moe::launch_prepare_router(wr, H, E, out, as_stream(stream)); });
 }
@@ -87,6 +96,7 @@ MOE_API moe_status moe_prepare_router_weights(const float* wr, int H, int E, voi
 namespace {
 moe_status check_router(const void* x, int x_dtype, const void* w_split, int T, int H, int E) {
   if (!x || !w_split) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(w_split)) return MOE_ERR_INVALID_ARG;
   if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (T < 1 || H < 1 || E < 1 || E > 1024 || H > (1 << 22)) return MOE_ERR_INVALID_ARG;
   const long long esz = x_dtype == MOE_DT_F32 ? 4 : 2;
@@ -98,7 +108,7 @@ moe_status check_router(const void* x, int x_dtype, const void* w_split, int T, 
 
 MOE_API moe_status moe_router_logits(const void* x, int x_dtype, const void* w_split, const float* bias, int T,
                                      int H, int E, float* logits, void* stream) {
-  if (!logits) return MOE_ERR_INVALID_ARG;
+  if (!logits || !al4(logits) || !al4(bias)) return MOE_ERR_INVALID_ARG;
   const moe_status st = check_router(x, x_dtype, w_split, T, H, E);
   if (st != MOE_OK) return st;
   return enqueue([&] { return moe::launch_router_logits(x, x_dtype, w_split, bias, T, H, E, logits, as_stream(stream)); });
@@ -108,6 +118,7 @@ MOE_API moe_status moe_route_hidden(const void* x, int x_dtype, const void* w_sp
                                     int E, int k, float* logits, int32_t* topk_ids, float* topk_w, int32_t* blob,
                                     void* stream) {
   if (!logits || !blob || (topk_ids == nullptr) != (topk_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!al4(logits) || !al4(bias) || !al4(blob) || !al4(topk_ids) || !al4(topk_w)) return MOE_ERR_INVALID_ARG;
   const moe_status st = check_router(x, x_dtype, w_split, T, H, E);
   if (st != MOE_OK) return st;
   if (k < 1 || k > 64 || k > E || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
@@ -127,6 +138,7 @@ MOE_API moe_status moe_permute(const int32_t* blob, int T, int k, int e_first, i
                                int32_t* sorted_pairs, int32_t* group_offsets, int32_t* pair_pos,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (!blob || !sorted_pairs || !group_offsets || !pair_pos) return MOE_ERR_INVALID_ARG;
+  if (!al4(blob) || !al4(sorted_pairs) || !al4(group_offsets) || !al4(pair_pos)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
   if (e_local < 1 || e_local > 1024 || e_first < 0 || !fits_i32((long long)e_first + e_local))
     return MOE_ERR_INVALID_ARG;
@@ -151,6 +163,9 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
   const bool w8 = a->wfmt == MOE_W_FP8_E4M3;
   if (!a->a || !a->group_offsets || !a->w0 || !a->out) return MOE_ERR_INVALID_ARG;
   if (gu ? !a->w1 : a->w1 != nullptr) return MOE_ERR_INVALID_ARG;
+  if (!al16(a->a) || !al16(a->w0) || !al16(a->w1) || !al16(a->s0) || !al16(a->s1) || !al16(a->out) ||
+      !al4(a->group_offsets) || !al4(a->row_index))
+    return MOE_ERR_INVALID_ARG;
   if (a->K < 64 || a->K % 64 != 0 || a->N < 64) return MOE_ERR_INVALID_ARG;
   if (a->N % (gu ? 64 : 128) != 0) return MOE_ERR_INVALID_ARG;
   if (a->n_groups < 1 || a->n_groups > 1024) return MOE_ERR_INVALID_ARG;
@@ -190,7 +205,7 @@ MOE_API moe_status moe_grouped_gemm(const moe_gemm_args* a, void* stream) {
 
 MOE_API moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N, int dtype, void* out,
                                              void* stream) {
-  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  if (!w || !out || !al16(w) || !al16(out)) return MOE_ERR_INVALID_ARG;
   if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (E < 1 || K < 1 || N < 1 || E > 65535 || K > (1 << 22) || (long long)E * K * N >= (1LL << 40))
     return MOE_ERR_INVALID_ARG;
@@ -198,7 +213,7 @@ MOE_API moe_status moe_prepare_dense_weights(const void* w, int E, int K, int N,
 }
 
 MOE_API moe_status moe_prepare_dense_weights_f16(const void* w, int E, int K, int N, void* out, void* stream) {
-  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  if (!w || !out || !al16(w) || !al16(out)) return MOE_ERR_INVALID_ARG;
   if (E < 1 || K < 1 || N < 1 || E > 65535 || K > (1 << 22) || (long long)E * K * N >= (1LL << 40))
     return MOE_ERR_INVALID_ARG;
   return enqueue([&] { return moe::launch_prepare(w, E, K, N, MOE_DT_F16, out, as_stream(stream)); });
@@ -208,6 +223,7 @@ MOE_API moe_status moe_combine(const void* expert_out, int expert_rows, int act_
                                const int32_t* pair_pos, const void* shared_out, int T, int k, int H,
                                void* y, int y_dtype, void* stream) {
   if (!expert_out || !blob || !pair_pos || !y) return MOE_ERR_INVALID_ARG;
+  if (!al16(expert_out) || !al16(shared_out) || !al16(y) || !al4(blob) || !al4(pair_pos)) return MOE_ERR_INVALID_ARG;
   if (!is_dtype(act_dtype)) return MOE_ERR_UNSUPPORTED;
   if (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (expert_rows < 1 || T < 1 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MOE_ERR_INVALID_ARG;

@@ -54,6 +54,8 @@ MOE_API moe_status moe_permute_noalloc(const int32_t* blob, int T, int k, int e_
                                        void* stream) {
   using moe::fits_i32;
   if (!blob || !sorted_pairs || !group_offsets || !pair_pos) return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)blob | (uintptr_t)sorted_pairs | (uintptr_t)group_offsets | (uintptr_t)pair_pos) & 3)
+    return MOE_ERR_INVALID_ARG;                    // int32 arrays: 4-byte aligned
   if (T < 1 || k < 1 || k > 64 || !fits_i32((long long)T * k)) return MOE_ERR_INVALID_ARG;
   if (e_local < 1 || e_local > 1024 || e_first < 0 || !fits_i32((long long)e_first + e_local))
     return MOE_ERR_INVALID_ARG;

@@ -22,13 +22,20 @@
  *   - Arguments are validated on the host before anything is enqueued; an invalid call returns
  *     MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED and enqueues nothing.  A failed launch returns
  *     MOE_ERR_HIP.  Validation needs no GPU.
+ *   - Alignment: int32 arrays (ids, blob, sorted_pairs, group_offsets, pair_pos, row_index) and
+ *     fp32 vectors and logits (topk_w, logits, bias) 4-byte aligned; matrices that kernels move 16
+ *     bytes at a time (activations x and h, expert and router weights and their scales, the
+ *     outputs of moe_grouped_gemm, expert_out, shared_out and y of moe_combine, prepared weight
+ *     copies, workspaces) 16-byte aligned.  A misaligned pointer is MOE_ERR_INVALID_ARG.
+ *     hipMalloc and PyTorch allocations satisfy both.
  *   - Data-dependent preconditions are not checked on the device: logits are finite, blob ids are
  *     in [0, E).  Kernels clamp every index they read, so violating them gives wrong values, not
  *     out-of-bounds accesses.
  *   - Row-major layouts; "bf16" is IEEE bfloat16 stored in 16 bits; conversions to bf16 round to
  *     nearest even.  No call depends on the number of local pairs being known on the host.
- *   - The library's only global state is a per-device cache of the compute-unit count; calls on
- *     different streams may run concurrently.
+ *   - The library's global state is a per-device cache of the compute-unit count and the
+ *     per-device scratch array of moe_permute_noalloc; calls on different streams may run
+ *     concurrently, except moe_permute_noalloc calls on one GPU (see its declaration).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

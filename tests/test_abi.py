@@ -256,6 +256,60 @@ def test_router_entry_points_validation(L):
     assert L.moe_route_hidden(F, 0, F, None, 8, 64, 1025, 2, F, F, F, F, None) == INV
 
 
+def test_misaligned_pointers_are_invalid(L):
+    """Each pointer argument one alignment unit off (2 bytes for 4-byte arrays, 8 bytes for
+    16-byte ones) is rejected before any HIP call; the aligned call differs only there."""
+    F, A2, A8 = FAKE, FAKE + 2, FAKE + 8
+    # moe_route(logits, T, E, k, ids, w, stream)
+    for i in (0, 4, 5):
+        args = [F, 8, 16, 2, F, F, None]
+        args[i] = A2
+        assert L.moe_route(*args) == INV, i
+    # moe_route_packed(logits, T, E, k, ids, w, blob, stream)
+    for i in (0, 4, 5, 6):
+        args = [F, 8, 16, 2, F, F, F, None]
+        args[i] = A2
+        assert L.moe_route_packed(*args) == INV, i
+    for i in (0, 1, 4):
+        args = [F, F, 4, 2, F, None]
+        args[i] = A2
+        assert L.moe_pack_routing(*args) == INV, i
+    ws = L.moe_permute_workspace_bytes(2049, 8, 8)
+    for i in (0, 5, 6, 7):
+        args = [F, 2049, 8, 0, 8, F, F, F, F, ws, None]
+        args[i] = A2
+        assert L.moe_permute(*args) == INV, i
+        noalloc = [F, 2049, 8, 0, 8, F, F, F, None]
+        noalloc[i] = A2
+        assert L.moe_permute_noalloc(*noalloc) == INV, i
+    for f in ("a", "w0", "w1", "out"):
+        assert L.moe_grouped_gemm(ctypes.byref(_gemm(**{f: A8})), None) == INV, f
+    for f in ("row_index", "group_offsets"):
+        assert L.moe_grouped_gemm(ctypes.byref(_gemm(**{f: A2})), None) == INV, f
+    q4 = dict(wfmt=1, out_dtype=2, group_size=128)
+    assert L.moe_grouped_gemm(ctypes.byref(_gemm(s0=A8, s1=F, **q4)), None) == INV
+    assert L.moe_grouped_gemm(ctypes.byref(_gemm(s0=F, s1=A8, **q4)), None) == INV
+    # moe_combine(expert_out, rows, act, blob, pair_pos, shared_out, T, k, H, y, y_dtype, stream)
+    for i, v in ((0, A8), (3, A2), (4, A2), (5, A8), (9, A8)):
+        args = [F, 64, 1, F, F, None, 8, 2, 256, F, 1, None]
+        args[i] = v
+        assert L.moe_combine(*args) == INV, i
+    assert L.moe_prepare_dense_weights(A8, 2, 64, 64, 1, F, None) == INV
+    assert L.moe_prepare_dense_weights(F, 2, 64, 64, 1, A8, None) == INV
+    assert L.moe_prepare_dense_weights_f16(A8, 2, 64, 64, F, None) == INV
+    assert L.moe_prepare_dense_weights_f16(F, 2, 64, 64, A8, None) == INV
+    assert L.moe_prepare_router_weights(A2, 64, 8, F, None) == INV
+    assert L.moe_prepare_router_weights(F, 64, 8, A8, None) == INV
+    for i, v in ((0, A8), (2, A8), (3, A2), (7, A2)):
+        args = [F, 1, F, None, 8, 64, 16, F, None]
+        args[i] = v
+        assert L.moe_router_logits(*args) == INV, i
+    for i, v in ((0, A8), (2, A8), (3, A2), (8, A2), (9, A2), (10, A2), (11, A2)):
+        args = [F, 1, F, None, 8, 64, 16, 2, F, F, F, F, None]
+        args[i] = v
+        assert L.moe_route_hidden(*args) == INV, i
+
+
 def test_weight_format_rule():
     """The bf16 / W4A16 choice by rows per expert (host logic): int4 where the expert weights are
     streamed (decode), bf16 where the matrix units bind (skewed hot experts)."""
