@@ -1550,6 +1550,7 @@ hipError_t run_dma(const GemmParams& p, hipStream_t s) {
 template <bool GU, bool NK>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
   constexpr int BM = 32, BN = 64, KC = 32, NW = GU ? 2 : 1;
+  constexpr int NC = BN / 16;                      // output columns per thread (tx + 16 c)
   __shared__ float sA[BM][KC + 1];
   __shared__ float sB[NW][BN][KC + 1];             // weight rows [n][k], padded
   extern __shared__ int tbl[];
@@ -1571,7 +1572,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
     const int local = tile - s_tstart[e];
     const int mt = local % mtiles, nt = local / mtiles;
     const int row0 = g0 + mt * BM, rows = min(BM, g1 - row0), n0 = nt * BN;
-    float acc[NW][2][4] = {};
+    float acc[NW][2][NC] = {};
     // source rows of this thread's activation elements (fixed for the tile)
     constexpr int A_PER = BM * KC / 256, B_PER = NW * KC * BN / 256;
     const float* a_src[A_PER];
@@ -1583,10 +1584,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
       src = min(max(src, 0), p.a_rows - 1);
       a_src[u] = A + (size_t)src * p.K + (tid + 256 * u) % KC;
     }
-    for (int k0 = 0; k0 < p.K; k0 += KC) {
-      // all loads of the chunk are issued before the first LDS store (consecutive threads read
-      // contiguous memory)
-      float av[A_PER], bv[B_PER];
+    // chunk loads (consecutive threads read contiguous memory); the next chunk's are issued
+    // before the current chunk's products, so their latency overlaps them
+    float av[A_PER], bv[B_PER];
+    auto load = [&](int k0) {
 #pragma unroll
       for (int u = 0; u < A_PER; ++u) av[u] = a_src[u][k0];
 #pragma unroll
@@ -1597,6 +1598,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
         if constexpr (NK) bv[u] = W[((size_t)e * p.N + n0 + v / KC) * p.K + k0 + v % KC];
         else bv[u] = W[((size_t)e * p.K + k0 + v / BN) * p.N + n0 + v % BN];
       }
+    };
+    load(0);
+    for (int k0 = 0; k0 < p.K; k0 += KC) {
 #pragma unroll
       for (int u = 0; u < A_PER; ++u) sA[(tid + 256 * u) / KC][(tid + 256 * u) % KC] = av[u];
 #pragma unroll
@@ -1607,12 +1611,13 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
         else sB[m][v % BN][v / BN] = bv[u];
       }
       __syncthreads();
+      if (k0 + KC < p.K) load(k0 + KC);
       for (int kk = 0; kk < KC; ++kk) {
         const float a0 = sA[ty][kk], a1 = sA[ty + 16][kk];
 #pragma unroll
         for (int m = 0; m < NW; ++m)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < NC; ++c) {
             const float b = sB[m][tx + 16 * c][kk];
             acc[m][0][c] = fmaf(a0, b, acc[m][0][c]);
             acc[m][1][c] = fmaf(a1, b, acc[m][1][c]);
@@ -1625,7 +1630,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
       const int row = ty + 16 * h;
       if (row >= rows) continue;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NC; ++c) {
         float v;
         if constexpr (GU) v = silu_mul(acc[0][h][c], acc[1][h][c]);
         else v = acc[0][h][c];
