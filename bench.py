@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import platform
@@ -63,11 +64,16 @@ DESCR = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library's sources with comments and whitespace removed: counter profiles taken on
+    other code are not reported, edits of comments alone do not invalidate them."""
     from expert_grouped_gemm_softmax_amd.build import sources
     h = hashlib.sha256()
     for p in sources() + [os.path.join(ROOT, "expert_grouped_gemm_softmax_amd", "csrc", "common.h")]:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                    # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

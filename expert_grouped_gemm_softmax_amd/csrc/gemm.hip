@@ -9,8 +9,8 @@
 //
 // Design (MI355X):
 //  - Work unit = tile (expert e, m-tile of BM rows of that expert, n-tile of BN output columns).
-//    Tiles are numbered expert by expert, n-tile major and m-tile minor, so consecutive tiles
-//    reuse one weight slab.  Each workgroup derives the tile table from group_offsets in LDS, so
+//    Tiles are numbered expert by expert, in groups of up to four m-tiles with the m-tile fastest,
+//    so consecutive tiles reuse one weight slab and a few activation tiles.  Each workgroup derives the tile table from group_offsets in LDS, so
 //    the number of local pairs never goes through the host.
 //  - Persistent grid, a multiple of 8 workgroups.  Workgroup b runs on XCD b % 8; the tiles are
 //    cut into 8 contiguous ranges and XCD x's workgroups walk range x, so tiles sharing a weight
@@ -19,16 +19,20 @@
 //    (W[e][n][k], K-contiguous: MOE_W_DENSE_NK) are copied into LDS the same way: 16 bytes per
 //    lane, 8 lanes per 128-byte row chunk, giving [row][k] tiles whose rows are what the MFMA
 //    operands read (8 consecutive k per lane).
-//    int4 words [e][k/8][n] hold 8 consecutive k of one column: they are dequantised
-//    (q * scale, rounded to bf16) into the same [n][k] LDS layout.
+//    int4 words [e][k/8][n] hold 8 consecutive k of one column: they are dequantised exactly to
+//    fp16 into the same [n][k] LDS layout (each 16-byte chunk's eight k in the order the
+//    dequantisation produces, the activations of those tiles reordered to match); fp8 bytes are
+//    converted exactly to bf16 or fp16.
 //  - 16x16x32 MFMA with fp32 accumulators; SwiGLU fused in the epilogue (each lane holds the gate
 //    and the up value of the same output element).  Operands are bf16 (dense bf16 weights) or
 //    fp16: int4 weights are dequantised exactly to fp16 (q * s has at most 11 significant bits;
 //    a bf16 tile would round it), bf16 activations feeding them are converted to fp16 on their
 //    way to LDS, and the down projection reads the fp16 SwiGLU output with fp16 weights.  fp16
 //    weights carry a factor 2^8 that the epilogue removes.
-//  - Global loads run ahead of the MFMAs through registers (one or two chunks) and one or two
-//    LDS buffers.
+//  - Decode-shaped tiles: global loads run ahead of the MFMAs through registers (two to four
+//    chunks) into one or two LDS buffers.  Prefill-shaped dense tiles: chunks are copied global ->
+//    LDS by the load unit (two or three buffers), or, for gate/up tiles whose weights no other
+//    tile reads, the weights go through registers two chunks ahead.
 #include "common.h"
 
 namespace moe {
