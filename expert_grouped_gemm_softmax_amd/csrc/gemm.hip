@@ -1888,10 +1888,14 @@ hipError_t launch_router_logits(const void* x, int x_dtype, const void* w_split,
   p.s0 = p.s1 = nullptr; p.out = logits; p.bias = bias;
   p.K = H; p.N = E; p.n_groups = 1; p.rows_cap = T; p.a_rows = T; p.row_div = 1; p.group_size = H;
   // 256-row tiles (64 experts wide) when they give every compute unit about one tile, else
-  // 32-row tiles, four workgroups per compute unit
+  // 16-row tiles, four workgroups per compute unit, four chunks in registers: with few tiles each
+  // workgroup's chain of K chunks is the time, and deeper loads shorten it (decode shape 32.6 ->
+  // 27.1 us against 32-row tiles with two chunks)
   const long long big_tiles = (long long)((T + 255) / 256) * (E / 64);
   if (2 * big_tiles >= device_cu_count())
     return run_bf16<Cfg<256, 64, 4, 1, 2, true, false, 1, 2, false, false, true>, float>(p, 1, s);
+  if (H % 256 == 0)
+    return run_bf16<Cfg<16, 64, 1, 4, 1, true, false, 4, 4, false, false, true>, float>(p, 4, s);
   return run_bf16<Cfg<32, 64, 1, 4, 1, true, false, 4, 2, false, false, true>, float>(p, 4, s);
 }
 

@@ -585,6 +585,23 @@ def _upload_x(inp, cfg):
     return torch.from_numpy(inp["x"]).to(_dev())
 
 
+@pytest.mark.parametrize("T,H,E", [(100, 512, 128), (100, 320, 128), (37, 4096, 64), (1, 256, 64)])
+def test_router_logits_small_batches(T, H, E):
+    """The projection's small-batch tiles (16 rows with four chunks in registers when H is a
+    multiple of 256, else 32 rows with two), every logit within the bound moe.h states."""
+    cfg = W.MoEConfig("router", T=T, H=H, E=E, k=2, I=64, e_first=0, e_local=1)
+    inp, x, wr, bias = _router_case(cfg)
+    logits = ops.router_logits(x, ops.prepare_router_weights(wr), bias=bias)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(inp["x"], inp["w_router"], inp.get("router_bias"))
+    xf = W.bf16_bits_to_f32(inp["x"])
+    absum = np.abs(xf.astype(np.float64)) @ np.abs(inp["w_router"].astype(np.float64))
+    bound = (2.0 ** -18 + (H // 32 + 32 + 2) * 2.0 ** -24) * absum + 2 * np.spacing(np.abs(ref).astype(np.float32))
+    err = np.abs(_np(logits).astype(np.float64) - ref)
+    print(f"router T={T} H={H} E={E}: max err/bound {np.max(err / bound):.3f}")
+    assert np.all(err <= bound)
+
+
 @pytest.mark.parametrize("name", list(W.CONFIGS))
 def test_router_projection_and_routing_from_hidden_states(name):
     """moe_route_hidden on every workload: each logit within the derived error bound of the
