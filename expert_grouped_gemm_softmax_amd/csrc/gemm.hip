@@ -1548,19 +1548,22 @@ hipError_t run_dma(const GemmParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// fp32 kernel (vector ALU): 32 x 64 tiles, K chunks of 32 staged in LDS.
+// fp32 kernel: 32 x 64 tiles, K chunks of 32 staged in LDS, fp32 MFMA (16x16x4) with fp32 accumulation.
 // ---------------------------------------------------------------------------------------------
 // NK: weights stored [e][n][k] (MOE_W_DENSE_NK), else [e][k][n] (MOE_W_DENSE).
 template <bool GU, bool NK>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
   constexpr int BM = 32, BN = 64, KC = 32, NW = GU ? 2 : 1;
-  constexpr int NC = BN / 16;                      // output columns per thread (tx + 16 c)
   __shared__ float sA[BM][KC + 1];
   __shared__ float sB[NW][BN][KC + 1];             // weight rows [n][k], padded
   extern __shared__ int tbl[];
   int* s_tstart = tbl;
   int* s_goff = tbl + (p.n_groups + 1);
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  // MFMA 16x16x4 fp32: wave w computes output columns 16 w .. 16 w + 15 of both 16-row blocks;
+  // lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] of each 4-k step and holds rows
+  // 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16 of the result
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
   const int tiles_n = p.N / BN;
   build_tile_table(p, BM, tiles_n, s_tstart, s_goff);
   __syncthreads();
@@ -1576,7 +1579,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
     const int local = tile - s_tstart[e];
     const int mt = local % mtiles, nt = local / mtiles;
     const int row0 = g0 + mt * BM, rows = min(BM, g1 - row0), n0 = nt * BN;
-    float acc[NW][2][NC] = {};
+    f32x4 acc[NW][2];
+#pragma unroll
+    for (int m = 0; m < NW; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     // source rows of this thread's activation elements (fixed for the tile)
     constexpr int A_PER = BM * KC / 256, B_PER = NW * KC * BN / 256;
     const float* a_src[A_PER];
@@ -1616,31 +1621,29 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
       }
       __syncthreads();
       if (k0 + KC < p.K) load(k0 + KC);
-      for (int kk = 0; kk < KC; ++kk) {
-        const float a0 = sA[ty][kk], a1 = sA[ty + 16][kk];
 #pragma unroll
-        for (int m = 0; m < NW; ++m)
+      for (int kk = 0; kk < KC; kk += 4) {
+        const float a0 = sA[li][kk + lk], a1 = sA[16 + li][kk + lk];
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const float b = sB[m][tx + 16 * c][kk];
-            acc[m][0][c] = fmaf(a0, b, acc[m][0][c]);
-            acc[m][1][c] = fmaf(a1, b, acc[m][1][c]);
-          }
+        for (int m = 0; m < NW; ++m) {
+          const float b = sB[m][16 * wave + li][kk + lk];
+          acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc[m][1], 0, 0, 0);
+        }
       }
       __syncthreads();
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = ty + 16 * h;
-      if (row >= rows) continue;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * h + 4 * lk + r;
+        if (row >= rows) continue;
         float v;
-        if constexpr (GU) v = silu_mul(acc[0][h][c], acc[1][h][c]);
-        else v = acc[0][h][c];
-        O[(size_t)(row0 + row) * p.N + n0 + tx + 16 * c] = v;
+        if constexpr (GU) v = silu_mul(acc[0][h][r], acc[1][h][r]);
+        else v = acc[0][h][r];
+        O[(size_t)(row0 + row) * p.N + n0 + 16 * wave + li] = v;
       }
-    }
   }
 }
 
