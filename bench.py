@@ -331,16 +331,16 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None, m
     t_start = time.perf_counter()
     for i in range(K):
         e = ev.get(i)
-        layer.step_route(logits, b)
+        layer.step_route(logits, b, stream)
         if e:
             e[0].record(stream)
-        layer.step_gate_up(x, b)
+        layer.step_gate_up(x, b, stream)
         if e:
             e[1].record(stream)
-        layer.step_down(x, b)
+        layer.step_down(x, b, stream)
         if cfg.shared_I:
-            layer.step_shared(x, b)
-        layer.step_combine(b)
+            layer.step_shared(x, b, stream)
+        layer.step_combine(b, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gu_us = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in sampled]))
@@ -357,9 +357,10 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None, m
 
     # Per-kernel breakdown, after the timed region (events between every step).
     names = ["route_pack_permute", "gate_up", "down"] + (["shared"] if cfg.shared_I else []) + ["combine"]
-    fns = [lambda: layer.step_route(logits, b), lambda: layer.step_gate_up(x, b),
-           lambda: layer.step_down(x, b)] + ([lambda: layer.step_shared(x, b)] if cfg.shared_I else []) + \
-          [lambda: layer.step_combine(b)]
+    fns = [lambda: layer.step_route(logits, b, stream), lambda: layer.step_gate_up(x, b, stream),
+           lambda: layer.step_down(x, b, stream)] + \
+          ([lambda: layer.step_shared(x, b, stream)] if cfg.shared_I else []) + \
+          [lambda: layer.step_combine(b, stream)]
     nb = max(3, min(K, 10))
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nb)]
     for i in range(nb):
@@ -375,7 +376,8 @@ def measure(name: str, steps: int, warmup: int, cpu_s: float | None, att=None, m
     # without an event's dispatch wait in front of each launch (which inflates a bracketed
     # 100-us kernel by several percent; the kernel traces agree with these figures).
     b2b = {}
-    for n, fn in (("gate_up", lambda: layer.step_gate_up(x, b)), ("down", lambda: layer.step_down(x, b))):
+    for n, fn in (("gate_up", lambda: layer.step_gate_up(x, b, stream)),
+                  ("down", lambda: layer.step_down(x, b, stream))):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(10):

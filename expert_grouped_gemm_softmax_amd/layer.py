@@ -243,6 +243,8 @@ class MoELayer:
         T = x.shape[0]
         assert x.dtype == self.act_dtype and tuple(logits.shape) == (T, self.E)
         b = self.buffers(T, x.device)
+        if stream is None:                        # looked up once: each lookup costs microseconds
+            stream = torch.cuda.current_stream()
         self.step_route(logits, b, stream)
         self.step_gate_up(x, b, stream)
         self.step_down(x, b, stream)
